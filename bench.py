@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark: per-token weight sweep of 64 synthetic 27B-shaped decoder
+layers (q, k, v, o, gate, up, down; 10.16 GB of PN-packed weights), M = 1,
+on one MI355X.
+
+A step is one token: every one of the 448 GEMVs, each with its own fp16
+input, all inputs resident in HBM before timing starts.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--schedule token|layer|gemv]
+                  [--config 3|4] [--no-cpu-baseline]
+
+value = algorithmic bytes per token (packed weights + fp16 inputs + fp32
+outputs) / step time, in GB/s; tokens/s is reported beside it.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "PN GEMV achieved HBM GB/s (% of peak) + 27B-shaped layer-sweep tokens/s"
+PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
+KERNEL_SOURCES = ["bit_quantized_decode_pn3t_amd/csrc/pn_kernels.hip",
+                  "bit_quantized_decode_pn3t_amd/csrc/pn_device.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from committed rocprofv3 counters, if they were
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("kernel_hash") != kernel_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(layers, threads):
+    """The oracle (fp64 decode + GEMV, C, OpenMP over rows) on a bounded
+    sample of the sweep: the first `layers` layers, scaled to one token."""
+    from bit_quantized_decode_pn3t_amd import synth
+    from oracle import pnref
+
+    used = pnref.set_threads(threads)
+    recs = synth.sweep_matrices(layers=layers, threads=threads)
+    sample_bytes = sum(r["W"].nbytes for r in recs)
+    pnref.gemv_f64(recs[0]["type"], recs[0]["W"][:64], 64, recs[0]["K"], recs[0]["x"])  # warm
+    t0 = time.perf_counter()
+    for r in recs:
+        pnref.gemv_f64(r["type"], r["W"], r["N"], r["K"], r["x"])
+    dt = time.perf_counter() - t0
+    return dt, sample_bytes, used
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--schedule", default="token", choices=["token", "layer", "gemv"])
+    ap.add_argument("--config", type=int, default=3, choices=[3, 4])
+    ap.add_argument("--layers", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the other schedules")
+    ap.add_argument("--cpu-layers", type=int, default=16)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from bit_quantized_decode_pn3t_amd import _binding as B
+    from bit_quantized_decode_pn3t_amd import sweep as S
+    from bit_quantized_decode_pn3t_amd import synth
+
+    torch.cuda.set_device(0)
+    m = None if args.config == 3 else 8
+    schedule = args.schedule if m is None else "gemv"
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+
+    t0 = time.perf_counter()
+    log("generating %d layers (M=%s) with %d threads" % (args.layers, m or 1, threads))
+    sw = S.Sweep(layers=args.layers, m=m, threads=threads)
+    torch.cuda.synchronize()
+    bytes_per_token = sw.weight_bytes + sw.act_bytes
+    log("resident: %.3f GB weights, %d matrices, %.1f s" % (sw.weight_bytes / 1e9, len(sw.mats),
+                                                            time.perf_counter() - t0))
+
+    def run_timed(sched, steps, warmup, per_step_events):
+        use_graph = sched in ("layer", "gemv")
+        g = sw.capture(sched) if use_graph else None
+        if not use_graph:
+            sw.prepare(sched)
+        stream = torch.cuda.current_stream()
+
+        def one():
+            if g is not None:
+                g.replay()
+            else:
+                sw.step(sched)
+
+        for _ in range(warmup):
+            one()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)] if per_step_events else []
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for i in range(steps):
+            if per_step_events:
+                evs[i][0].record(stream)
+            one()
+            if per_step_events:
+                evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+        ev_ms = [a.elapsed_time(b) for a, b in evs]
+        return wall, ev_ms, B.pn_variant_name(B.pn_last_variant())
+
+    log("timing %d steps (%d warmup), schedule %s" % (args.steps, args.warmup, schedule))
+    wall, ev_ms, variant = run_timed(schedule, args.steps, args.warmup,
+                                     per_step_events=(schedule == "token"))
+    ms_per_step = wall / args.steps * 1e3
+    value = bytes_per_token / (wall / args.steps) / 1e9
+    tok_s = args.steps / wall
+
+    workload = "sweep64_m%d_%s" % (m or 1, schedule)
+    if schedule == "token":
+        # one launch per step: the events bracket exactly the dominant kernel
+        kern_ms = sum(ev_ms) / len(ev_ms)
+        achieved = bytes_per_token / (kern_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_GBPS, 4), "traffic": measured_traffic(workload),
+                    "kernel": "gemv_stream", "kernel_avg_ms": round(kern_ms, 4),
+                    "algorithmic_bytes_per_launch": bytes_per_token}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(value, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(value / PEAK_GBPS, 4), "traffic": measured_traffic(workload),
+                    "kernel": variant, "note": "step wall time over %d launches" % sw.launches(schedule)}
+
+    launches = sw.launches(schedule)
+    secondary = {}
+    if not args.no_secondary and m is None:
+        for other in ("layer", "gemv"):
+            if other == schedule:
+                continue
+            w2, _, _ = run_timed(other, args.steps, 2, False)
+            secondary[other] = {"tokens_per_s": round(args.steps / w2, 2),
+                                "gbps": round(bytes_per_token / (w2 / args.steps) / 1e9, 1),
+                                "launches_per_token": sw.launches(other)}
+            log("schedule %s: %.1f tok/s" % (other, args.steps / w2))
+    sw.close()
+    del sw
+    torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline and m is None:
+        log("cpu baseline: oracle on %d layers, %d threads" % (args.cpu_layers, threads))
+        dt, sample_bytes, used = cpu_baseline(args.cpu_layers, threads)
+        weights_per_token = sum(synth.row_bytes(t, k) * n for _, t, n, k in synth.SWEEP_LAYER) * args.layers
+        token_fraction = sample_bytes / weights_per_token
+        cpu = {"value": round(token_fraction / dt, 4), "unit": "tok/s", "cores": used, "kind": "oracle",
+               "sample": "first %d of %d layers (%.2f GB packed, %.1f%% of a token) in %.2f s; "
+                         "fp64 decode+GEMV, OpenMP over rows" % (args.cpu_layers, args.layers,
+                                                                sample_bytes / 1e9, 100 * token_fraction, dt),
+               "gbps_packed": round(sample_bytes / dt / 1e9, 3)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "pn3t/pn4t weights, fp16 activations, fp32 accumulate",
+        "data": "synthetic (seeded random codes and fp16 scales; fp16 N(0,1) activations)",
+        "config": {"workload": "64-layer 27B-shaped sweep, M=%d, %s schedule" % (m or 1, schedule),
+                   "layers": args.layers, "gemvs_per_token": 7 * args.layers,
+                   "bytes_per_token": bytes_per_token, "schedule": schedule,
+                   "launches_per_token": launches},
+        "tokens_per_s": round(tok_s, 2),
+        "frac_of_peak": round(value / PEAK_GBPS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "other_schedules": secondary,
+        "kernel_hash": kernel_hash(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

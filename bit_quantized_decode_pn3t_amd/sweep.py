@@ -1,0 +1,123 @@
+"""Per-token weight sweep over a 27B-shaped decoder stack (64 layers x
+q, k, v, o, gate, up, down), the decode workload of the tensorless pages
+("Why the P100", "Why memory bandwidth sets the pace": every weight is read
+once per token).
+
+The executor places every packed matrix in HBM once, then runs one token's
+GEMVs on the current stream in one of these launch schedules:
+  token  one grouped launch for all GEMVs of the token (pn_group_run);
+  layer  four launches per layer, the groups a real decoder can form because
+         their inputs are ready together: {q, k, v}, {o}, {gate, up}, {down};
+  gemv   one pn_gemv launch per matrix.
+With M > 1 every matrix is one pn_gemm_smallm launch.  A schedule can be
+captured once into a HIP graph (torch.cuda.CUDAGraph) and replayed.
+"""
+import numpy as np
+import torch
+
+from . import _binding as B
+from . import synth
+
+LAYER_GROUPS = ((0, 1, 2), (3,), (4, 5), (6,))
+
+
+class Sweep:
+    def __init__(self, layers=synth.SWEEP_LAYERS, m=None, device="cuda", threads=16,
+                 sample=None):
+        """Generate and upload the sweep.  `sample(rec)` (optional) sees each
+        matrix on the host before it is dropped, e.g. to keep some rows."""
+        self.layers = layers
+        self.m = m
+        self.device = torch.device(device)
+        self.mats = []
+        self.weight_bytes = 0
+        self.act_bytes = 0
+
+        def consume(rec):
+            if sample is not None:
+                sample(rec)
+            w = torch.from_numpy(rec["W"]).to(self.device)
+            x = torch.from_numpy(rec["x"]).to(self.device)
+            n = rec["N"]
+            y = torch.empty((n,) if m is None else (m, n), dtype=torch.float32, device=self.device)
+            self.mats.append(dict(name=rec["name"], layer=rec["layer"], mat=rec["mat"], type=rec["type"],
+                                  N=n, K=rec["K"], W=w, x=x, y=y))
+            self.weight_bytes += w.numel()
+            self.act_bytes += x.numel() * 2 + y.numel() * 4
+
+        synth.sweep_matrices(layers=layers, m=m, config=3 if m is None else 4, threads=threads,
+                             consume=consume)
+        self.groups = {}
+        self.graph = None
+
+    # -- schedules --------------------------------------------------------
+    def _problem(self, e):
+        return (e["type"], e["W"], e["N"], e["K"], e["x"], e["y"])
+
+    def prepare(self, schedule):
+        if self.m is not None and schedule != "gemv":
+            raise ValueError("M > 1 runs the gemv schedule only")
+        if schedule == "token" and "token" not in self.groups:
+            self.groups["token"] = [B.Group([self._problem(e) for e in self.mats])]
+        if schedule == "layer" and "layer" not in self.groups:
+            gl = []
+            per = len(synth.SWEEP_LAYER)
+            for l in range(self.layers):
+                for grp in LAYER_GROUPS:
+                    gl.append(B.Group([self._problem(self.mats[l * per + j]) for j in grp]))
+            self.groups["layer"] = gl
+
+    def launches(self, schedule):
+        if schedule in ("token", "layer"):
+            return len(self.groups[schedule])
+        return len(self.mats)
+
+    def step(self, schedule="layer"):
+        """Enqueue one token's GEMVs on the current stream."""
+        if schedule in ("token", "layer"):
+            self.prepare(schedule)
+            for g in self.groups[schedule]:
+                g.run()
+        elif schedule == "gemv":
+            if self.m is None:
+                for e in self.mats:
+                    B.pn_gemv(e["type"], e["W"], e["N"], e["K"], e["x"], e["y"])
+            else:
+                for e in self.mats:
+                    B.pn_gemm_smallm(e["type"], e["W"], e["N"], e["K"], e["x"], e["K"], self.m,
+                                     e["y"], e["N"])
+        else:
+            raise ValueError(schedule)
+
+    def capture(self, schedule="layer"):
+        """Capture one step into a HIP graph; returns the graph."""
+        if schedule in ("token", "layer"):
+            self.prepare(schedule)
+        self.step(schedule)  # warm: first launches, occupancy queries
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step(schedule)
+        torch.cuda.synchronize()
+        self.graph = g
+        return g
+
+    def outputs(self):
+        return [e["y"] for e in self.mats]
+
+    def close(self):
+        for gl in self.groups.values():
+            for g in gl:
+                g.close()
+        self.groups = {}
+        self.graph = None
+
+
+def sample_rows(rec, rows_per_matrix, store):
+    """A `sample` callback body: keep rows (first, last and seeded random ones)
+    and the activation of one matrix for later checks."""
+    n = rec["N"]
+    g = np.random.default_rng([rec["layer"], rec["mat"], 99])
+    rows = sorted(set([0, n - 1] + list(g.integers(0, n, size=max(rows_per_matrix - 2, 0)))))
+    store[(rec["layer"], rec["mat"])] = dict(rows=np.array(rows), W=rec["W"][rows].copy(),
+                                             x=rec["x"].copy(), type=rec["type"], K=rec["K"])

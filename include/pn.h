@@ -1,0 +1,142 @@
+/*
+ * pn.h - C ABI of the PN decode GEMV library for AMD Instinct MI355X (gfx950).
+ *
+ * The PN weight format (tensorless, "Why a P100-native weight format"):
+ *   - "Every block is 34 bytes": an fp16 scale d (2 bytes) followed by eight
+ *     32-bit code words.  pn3t packs ten 3-bit codes per word (80 weights per
+ *     block); pn4t packs eight 4-bit codes per word (64 weights per block).
+ *     "A row must hold a whole number of blocks": K is a multiple of 80 or 64.
+ *   - "Codes never straddle the two halves of a word": even codes sit in the
+ *     low 16 bits, odd codes in the high 16 bits, at the same offsets.
+ *   - "Exact decode in fp32": weight = d * (n - z), exact in binary32.
+ *   - "Zero is a code, and the scale has a sign": z = 4 for pn3t (range
+ *     -4..+3 steps); this library takes z = 8 for pn4t (-8..+7).
+ * Bit layout fixed by this library where the page is silent: scale at bytes
+ * 0-1 and word i at bytes 2+4i..5+4i, little-endian; word i holds the
+ * block's weights C*i .. C*i+C-1 (C = 10 or 8); weight j of a word sits in
+ * half (j & 1) at bit offset b*(j >> 1) from that half's lowest bit; pn3t
+ * bits 15 and 31 are ignored.
+ *
+ * Memory: every pointer is a DEVICE pointer owned by the caller (e.g. a torch
+ * tensor's data_ptr()).  Weight matrices are N rows of K/W blocks, rows
+ * contiguous (row stride pn_row_bytes(t, K)); the base only needs 2-byte
+ * alignment.  Activations are IEEE fp16, 4-byte aligned; outputs are fp32,
+ * 4-byte aligned, overwritten (never accumulated).
+ *
+ * Streams: `stream` is a hipStream_t (NULL = the default stream).  Calls
+ * enqueue work and return without synchronising; device faults surface at
+ * the caller's next synchronisation.  The calls allocate nothing (except
+ * pn_group_create, documented there) and are safe to call from several host
+ * threads at once.
+ *
+ * Errors: arguments are checked on the host before any launch; a failing
+ * check returns a negative pn_status and enqueues nothing.
+ */
+#ifndef PN_H
+#define PN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PN_PN3T = 0, PN_PN4T = 1 } pn_type;
+
+typedef enum {
+    PN_OK = 0,
+    PN_EINVAL = -1,       /* null pointer, unknown type, bad count          */
+    PN_ESHAPE = -2,       /* N < 1, K not a positive multiple of W, M/ld bad */
+    PN_EALIGN = -3,       /* W not 2-aligned, x/X/y/Y not 4-aligned         */
+    PN_EUNSUPPORTED = -4, /* shape outside what the kernels support         */
+    PN_ELAUNCH = -5,      /* the HIP launch or a HIP runtime call failed    */
+    PN_ENOMEM = -6        /* device allocation failed (pn_group_create)     */
+} pn_status;
+
+/* Weights per block: 80 (pn3t) or 64 (pn4t); 0 for an unknown type. */
+int pn_weights_per_block(pn_type t);
+
+/* Bytes of one packed row of K weights: (K / W) * 34, or 0 if K is not a
+ * positive multiple of W. */
+size_t pn_row_bytes(pn_type t, int64_t K);
+
+/* y[r] = sum_k w[r,k] * x[k] for r < N.
+ * "One lane, one word" and "Exact decode in fp32" on the pn-format page
+ * describe the decode GEMV this computes: weights decoded exactly as
+ * d * (n - z), products accumulated in fp32 (any order; the result is within
+ * 1e-5 * sum_k |w[r,k] x[k]| of the exact value, row by row).
+ *   W : N * pn_row_bytes(t, K) bytes, 2-byte aligned
+ *   x : K fp16 values, 4-byte aligned
+ *   y : N fp32 values, 4-byte aligned, overwritten */
+pn_status pn_gemv(pn_type t, const void *W, int64_t N, int64_t K,
+                  const void *x, float *y, void *stream);
+
+/* Two matrices of the same type and shape against one activation, one
+ * launch (the fused gate + up projection of a decoder layer):
+ * y0 = W0 x, y1 = W1 x.  Arguments as for pn_gemv. */
+pn_status pn_gemv2(pn_type t, const void *W0, const void *W1, int64_t N,
+                   int64_t K, const void *x, float *y0, float *y1, void *stream);
+
+/* Small-batch product for M <= 8 activation rows (speculative-decoding
+ * verification width; v100-skinny README, "How QPN works"):
+ * Y[m*ldy + r] = sum_k w[r,k] * X[m*ldx + k] for m < M, r < N.
+ * Each weight is decoded once and used M times.
+ *   X : M rows of fp16, leading dimension ldx >= K (elements), 4-byte aligned,
+ *       ldx even
+ *   Y : M rows of fp32, leading dimension ldy >= N (elements), overwritten
+ *   M : 1..8 */
+pn_status pn_gemm_smallm(pn_type t, const void *W, int64_t N, int64_t K,
+                         const void *X, int64_t ldx, int M,
+                         float *Y, int64_t ldy, void *stream);
+
+/* Dense fp32 copy of the decoded weights, out[r*K + k] = d * (n - z),
+ * bit-exact with the format's definition ("Exact decode in fp32": no
+ * rounding in decode, so every correct decoder gives the same bits).
+ *   out : N * K fp32, 4-byte aligned */
+pn_status pn_dequantize(pn_type t, const void *W, int64_t N, int64_t K,
+                        float *out, void *stream);
+
+/* A group of independent GEMVs run by one kernel launch (a decoder layer's
+ * projections, or a whole per-token weight sweep).  Each entry is one
+ * pn_gemv problem; the entries may mix types and shapes. */
+typedef struct pn_gemv_desc {
+    const void *W;   /* packed rows, device          */
+    const void *x;   /* fp16 [K], device             */
+    float *y;        /* fp32 [N], device, overwritten */
+    int64_t N;
+    int64_t K;
+    int32_t type;    /* pn_type                      */
+    int32_t reserved;
+} pn_gemv_desc;
+
+typedef struct pn_group pn_group;
+
+/* Validate `count` descriptors (host array) and build a launch plan.  This
+ * call allocates device memory for the plan's tables and copies them there
+ * synchronously; the plan holds the descriptors' device pointers, which must
+ * stay valid while the plan is used.  Returns PN_ENOMEM if allocation fails.
+ * Every problem's rows must be whole groups of 8 blocks (K a multiple of 640
+ * for pn3t, 512 for pn4t) with 2*K <= 64 KiB of activation; other shapes
+ * return PN_EUNSUPPORTED (pn_gemv takes them one at a time). */
+pn_status pn_group_create(const pn_gemv_desc *descs, int count, pn_group **out);
+
+/* Enqueue all GEMVs of the plan as one launch on `stream`. */
+pn_status pn_group_run(const pn_group *g, void *stream);
+
+/* Free a plan (NULL is allowed).  Synchronises the device first. */
+void pn_group_destroy(pn_group *g);
+
+/* Text for a status code. */
+const char *pn_status_str(pn_status e);
+
+/* Kernel variant chosen by this thread's last successful enqueue (a census
+ * for benchmarks so that no fallback route goes unreported); values are
+ * listed by pn_variant_name. */
+int pn_last_variant(void);
+const char *pn_variant_name(int v);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

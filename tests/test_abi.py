@@ -1,0 +1,95 @@
+"""The C-ABI library loads and exports every symbol include/pn.h declares;
+host-side argument checks fail with the documented status before any launch.
+CPU only: no call here reaches the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_quantized_decode_pn3t_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pn.h")
+
+PN_EINVAL, PN_ESHAPE, PN_EALIGN = -1, -2, -3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_binding_exports():
+    assert declared_functions() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        ctypes.cast(getattr(lib, name), ctypes.c_void_p)
+
+
+def test_host_helpers():
+    assert B.pn_weights_per_block("pn3t") == 80
+    assert B.pn_weights_per_block("pn4t") == 64
+    assert B.pn_weights_per_block(7) == 0
+    assert B.pn_row_bytes("pn3t", 5120) == 64 * 34
+    assert B.pn_row_bytes("pn4t", 17408) == 272 * 34
+    assert B.pn_row_bytes("pn4t", 6144) == 96 * 34
+    assert B.pn_row_bytes("pn3t", 6144) == 0
+    assert B.pn_row_bytes("pn3t", 0) == 0
+    assert "ok" in B.status_str(0)
+    assert B.pn_variant_name(B.pn_last_variant()) == "none"
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails its host checks
+
+
+@pytest.mark.parametrize("args,status", [
+    (("pn3t", None, 4, 80, FAKE, FAKE), PN_EINVAL),
+    ((9, FAKE, 4, 80, FAKE, FAKE), PN_EINVAL),
+    (("pn3t", FAKE, 0, 80, FAKE, FAKE), PN_ESHAPE),
+    (("pn3t", FAKE, 4, 81, FAKE, FAKE), PN_ESHAPE),
+    (("pn3t", FAKE, 4, 64, FAKE, FAKE), PN_ESHAPE),
+    (("pn4t", FAKE, 4, 0, FAKE, FAKE), PN_ESHAPE),
+    (("pn3t", FAKE + 1, 4, 80, FAKE, FAKE), PN_EALIGN),
+    (("pn3t", FAKE, 4, 80, FAKE + 2, FAKE), PN_EALIGN),
+    (("pn3t", FAKE, 4, 80, FAKE, FAKE + 2), PN_EALIGN),
+    (("pn3t", FAKE, 4, 80, None, FAKE), PN_EINVAL),
+])
+def test_gemv_host_checks(args, status):
+    assert B.pn_gemv(*args, stream=0, check=False) == status
+
+
+def test_other_entry_points_host_checks():
+    assert B.pn_gemv2("pn3t", FAKE, None, 4, 80, FAKE, FAKE, FAKE, stream=0, check=False) == PN_EINVAL
+    assert B.pn_gemv2("pn4t", FAKE, FAKE, 4, 80, FAKE, FAKE, FAKE, stream=0, check=False) == PN_ESHAPE
+    assert B.pn_gemm_smallm("pn3t", FAKE, 4, 80, FAKE, 80, 9, FAKE, 4, stream=0, check=False) == PN_ESHAPE
+    assert B.pn_gemm_smallm("pn3t", FAKE, 4, 80, FAKE, 80, 0, FAKE, 4, stream=0, check=False) == PN_ESHAPE
+    assert B.pn_gemm_smallm("pn3t", FAKE, 4, 80, FAKE, 79, 2, FAKE, 4, stream=0, check=False) == PN_ESHAPE
+    assert B.pn_gemm_smallm("pn3t", FAKE, 4, 80, FAKE, 81, 2, FAKE, 4, stream=0, check=False) == PN_ESHAPE
+    assert B.pn_gemm_smallm("pn3t", FAKE, 4, 80, FAKE, 80, 2, FAKE, 3, stream=0, check=False) == PN_ESHAPE
+    assert B.pn_dequantize("pn4t", FAKE, 4, 64, FAKE + 1, stream=0, check=False) == PN_EALIGN
+    assert B.pn_dequantize("pn4t", FAKE, 4, 100, FAKE, stream=0, check=False) == PN_ESHAPE
+    with pytest.raises(B.PNError):
+        B.pn_gemv("pn3t", FAKE, 4, 81, FAKE, FAKE, stream=0)
+
+
+def test_group_host_checks():
+    with pytest.raises(B.PNError) as e:
+        B.Group([("pn3t", FAKE, 4, 81, FAKE, FAKE)])
+    assert e.value.status == PN_ESHAPE
+    with pytest.raises(B.PNError) as e:
+        B.Group([("pn3t", FAKE, 4, 640, FAKE, FAKE), ("pn4t", FAKE + 1, 4, 512, FAKE, FAKE)])
+    assert e.value.status == PN_EALIGN
+    with pytest.raises(B.PNError) as e:  # rows of 3 blocks: not whole 8-block passes
+        B.Group([("pn3t", FAKE, 4, 240, FAKE, FAKE)])
+    assert e.value.status == -4
+    lib = B.lib()
+    h = ctypes.c_void_p()
+    assert lib.pn_group_create(None, 1, ctypes.byref(h)) == PN_EINVAL
+    assert lib.pn_group_run(None, None) == PN_EINVAL
+    lib.pn_group_destroy(None)
