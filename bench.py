@@ -82,7 +82,10 @@ def main():
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the other schedules")
-    ap.add_argument("--cpu-layers", type=int, default=16)
+    ap.add_argument("--cpu-layers", type=int, default=64)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run one device copy of this many MiB (a kernel of known traffic "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -97,6 +100,15 @@ def main():
     from bit_quantized_decode_pn3t_amd import synth
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: %d bytes read, %d written" % (n, n))
+        del src, dst
     m = None if args.config == 3 else 8
     schedule = args.schedule if m is None else "gemv"
     threads = max(1, min(16, len(os.sched_getaffinity(0))))

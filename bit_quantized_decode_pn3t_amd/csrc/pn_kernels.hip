@@ -28,7 +28,29 @@ using namespace pn;
 
 namespace {
 
-constexpr int kWaves = 4;               // waves per workgroup
+#ifndef PN_WAVES
+#define PN_WAVES 4
+#endif
+#ifndef PN_ROWS_PER_GROUP
+#define PN_ROWS_PER_GROUP 2
+#endif
+#ifndef PN_ITEMS_IN_FLIGHT
+#define PN_ITEMS_IN_FLIGHT 4
+#endif
+// Cache policy bits of the weight loads (2 = nontemporal).  Plain loads are
+// the default: the scale loads touch the cache lines the word loads just
+// fetched, and nontemporal word loads make those second touches miss.
+#ifndef PN_WEIGHT_AUX
+#define PN_WEIGHT_AUX 0
+#endif
+// With two words per lane, take the block scale from the words' own 12-byte
+// window (one dwordx3 load per lane and row instead of a dwordx2 and a
+// ushort).  Off by default: measured slower on MI355X.
+#ifndef PN_SCALE_IN_WINDOW
+#define PN_SCALE_IN_WINDOW 0
+#endif
+
+constexpr int kWaves = PN_WAVES;        // waves per workgroup
 constexpr int kThreads = 64 * kWaves;   // workgroup size
 constexpr int kMaxLdsBytes = 64 * 1024; // LDS the streaming kernels may use
 
@@ -52,6 +74,7 @@ struct Prob {
     int32_t nw;         // code words per row = 8 * K / W
     int32_t type;       // 0 = pn3t, 1 = pn4t
     int32_t tile0;      // first global tile index of this problem
+    int32_t rpw;        // rows per wave in this problem's tiles
 };
 
 // Kernel arguments: up to two problems inline (pn_gemv, pn_gemv2), or a
@@ -65,38 +88,32 @@ struct StreamArgs {
 
 // ---------------------------------------------------------------------------
 // Activation staging into LDS.  Word f of a row multiplies x[C*f .. C*f+C-1].
-// pn4t: LDS holds x as is (16 bytes per word).  pn3t: the first 8 values of
-// each word go to a 16-byte array and the last 2 to a 4-byte array, so that
-// every lane reads its word's activations with one ds_read_b128 and one
-// ds_read_b32, both naturally aligned and conflict-free.  Words past the end
-// of the row (a ragged last pass) read zeros.
+// With V words per lane, word f = V*j + v goes to slot v, entry j, so that
+// the 64 lanes of a pass read 64 consecutive 16-byte entries of one slot
+// (one conflict-free ds_read_b128 per word).  pn4t: entry = the word's 8
+// activations (16 bytes).  pn3t: the first 8 go to a 16-byte entry, the last 2
+// to a 4-byte entry in a second array (one ds_read_b128 + one ds_read_b32,
+// both aligned).  LDS bytes: 16*nw (+ 4*nw for pn3t) = 2*K.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void stage_x(const Prob &p, int nwp, uint8_t *lds)
+template <int V>
+__device__ __forceinline__ void stage_x(const Prob &p, uint8_t *lds)
 {
     const int nw = p.nw;
-    if (p.type == 0) {
-        uint4 *a = (uint4 *)lds;
-        uint32_t *b = (uint32_t *)(lds + 16 * nwp);
-        for (int f = threadIdx.x; f < nwp; f += kThreads) {
-            uint4 va = make_uint4(0, 0, 0, 0);
-            uint32_t vb = 0;
-            if (f < nw) {
-                const uint8_t *src = p.x + 20 * (size_t)f;
-                va = make_uint4(load_u32(src), load_u32(src + 4), load_u32(src + 8), load_u32(src + 12));
-                vb = load_u32(src + 16);
-            }
-            a[f] = va;
-            b[f] = vb;
-        }
-    } else {
-        uint4 *a = (uint4 *)lds;
-        for (int f = threadIdx.x; f < nwp; f += kThreads) {
-            uint4 va = make_uint4(0, 0, 0, 0);
-            if (f < nw) {
-                const uint8_t *src = p.x + 16 * (size_t)f;
-                va = make_uint4(load_u32(src), load_u32(src + 4), load_u32(src + 8), load_u32(src + 12));
-            }
-            a[f] = va;
+    const int per = nw / V;  // entries per slot
+    uint4 *a = (uint4 *)lds;
+    uint32_t *b = (uint32_t *)(lds + 16 * nw);
+    // Threads walk LDS entries in order (conflict-free stores); entry e of
+    // slot v holds word f = V * (e - v * per) + v.
+    for (int e = threadIdx.x; e < nw; e += kThreads) {
+        const int v = e / per;
+        const int f = V * (e - v * per) + v;
+        if (p.type == 0) {
+            const uint8_t *src = p.x + 20 * (size_t)f;
+            a[e] = make_uint4(load_u32(src), load_u32(src + 4), load_u32(src + 8), load_u32(src + 12));
+            b[e] = load_u32(src + 16);
+        } else {
+            const uint8_t *src = p.x + 16 * (size_t)f;
+            a[e] = make_uint4(load_u32(src), load_u32(src + 4), load_u32(src + 8), load_u32(src + 12));
         }
     }
 }
@@ -106,30 +123,45 @@ __device__ __forceinline__ uint32_t word_off(uint32_t f) { return 34u * (f >> 3)
 __device__ __forceinline__ uint32_t scale_off(uint32_t f) { return 34u * (f >> 3); }
 
 // One wave streams `nrows` consecutive rows of one problem (nrows <= 64),
-// R rows at a time, one code word per lane per row ("One lane, one word").
-// The loads form one continuous pipeline of "items" (R rows x one pass of 64
-// words = 8 blocks = 272 bytes per row) with U items in flight; prefetch runs
-// across row groups, so the load stream never drains until the wave's last
-// row.  All loads go through one buffer resource that covers the wave's valid
-// rows: rows past N read zeros (no clamping, no fault).  Finished row sums are
-// parked in lane (row - row0) of one register and stored once at the end.
-// Requires nw % 64 == 0 (K a multiple of 8 blocks).
-template <int TYPE, int R, int U>
-__device__ __forceinline__ void stream_wave(const Prob &p, int row0, int nrows, int nwp, const uint8_t *lds)
+// R rows at a time.  Lane l of a pass owns V consecutive code words of one
+// block ("One lane, one word", widened to V words so that one unaligned
+// buffer_load covers them and they share one scale).  The loads form one
+// continuous pipeline of "items" (R rows x one pass of 64*V words = 8*V
+// blocks) with U items in flight; prefetch runs across row groups, so the
+// load stream never drains until the wave's last row.  All loads go through
+// one buffer resource that covers the wave's valid rows: rows past N read
+// zeros (no clamping, no fault).  Finished row sums are parked in lane
+// (row - row0) of one register and stored once at the end.
+// Requires nw % (64 * V) == 0.
+template <int TYPE, int R, int U, int V>
+__device__ __forceinline__ void stream_wave(const Prob &p, int row0, int nrows, const uint8_t *lds)
 {
     constexpr int P = Unpack<TYPE>::kPairs;
-    constexpr int kPassBytes = 64 / kWordsPerBlock * kBlockBytes;  // 272
+    constexpr int kPassBytes = 8 * V * kBlockBytes;  // 272 * V
     const int lane = threadIdx.x & 63;
-    const int nfull = uniform(p.nw >> 6);
-    const int row_bytes = uniform((p.nw >> 3) * 34);
+    const int nw = uniform(p.nw);
+    const int npass = nw / (64 * V);
+    const int row_bytes = uniform((nw >> 3) * 34);
     const int valid = uniform(p.N - row0 < nrows ? p.N - row0 : nrows);
-    const int total = uniform(((nrows + R - 1) / R) * nfull);
+    const int total = uniform(((nrows + R - 1) / R) * npass);
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc(uniform_ptr(p.W + (size_t)row0 * row_bytes), (uint32_t)valid * (uint32_t)row_bytes);
-    const int wo = (int)word_off(lane), so = (int)scale_off(lane);
-    const int lds_lane = lane * 16;
+    const int wo = (int)word_off((uint32_t)(V * lane)), so = (int)scale_off((uint32_t)(V * lane));
+    const int per = nw / V;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 *lds_a = (const u32x4 *)lds + lane;
+    const uint32_t *lds_b = (const uint32_t *)(lds + 16 * nw) + lane;
+    // Scale in the words' window (V == 2): lane q = lane & 3 of a block owns
+    // words 2q and 2q+1 and loads 12 bytes at block offset 8q (q < 3) or 22
+    // (q = 3), always inside the block.  Its words start at window byte 2
+    // (q < 3) or 4 (q = 3); v_perm_b32 picks them with a per-lane selector,
+    // and lane q = 0 holds the block's scale in its first two bytes.
+    constexpr bool kSiw = V == 2 && PN_SCALE_IN_WINDOW;
+    const int q4 = lane & 3;
+    const int wwo = so + (q4 < 3 ? 8 * q4 : 22);
+    const uint32_t wsel = q4 < 3 ? 0x05040302u : 0x07060504u;
 
-    uint32_t qw[U][R], qs[U][R];
+    uint32_t qw[U][R][V], qs[U][R];
     float acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = 0.0f;
@@ -141,26 +173,55 @@ __device__ __forceinline__ void stream_wave(const Prob &p, int row0, int nrows, 
         const int soff = ig * R * row_bytes + ip * kPassBytes;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            qw[slot][r] = __builtin_amdgcn_raw_buffer_load_b32(rs, wo, soff + r * row_bytes, 0);
-            qs[slot][r] = __builtin_amdgcn_raw_buffer_load_b16(rs, so, soff + r * row_bytes, 0);
+            if constexpr (kSiw) {
+                const auto w3 = __builtin_amdgcn_raw_buffer_load_b96(rs, wwo, soff + r * row_bytes, PN_WEIGHT_AUX);
+                qw[slot][r][0] = w3[0];
+                qw[slot][r][V - 1] = w3[1];
+                qs[slot][r] = w3[2];
+            } else if constexpr (V == 1) {
+                qw[slot][r][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, wo, soff + r * row_bytes, PN_WEIGHT_AUX);
+                qs[slot][r] = __builtin_amdgcn_raw_buffer_load_b16(rs, so, soff + r * row_bytes, PN_WEIGHT_AUX);
+            } else {
+                const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(rs, wo, soff + r * row_bytes, PN_WEIGHT_AUX);
+                qw[slot][r][0] = v2[0];
+                qw[slot][r][V - 1] = v2[1];
+                qs[slot][r] = __builtin_amdgcn_raw_buffer_load_b16(rs, so, soff + r * row_bytes, PN_WEIGHT_AUX);
+            }
         }
-        if (++ip == nfull) { ip = 0; ++ig; }
+        if (++ip == npass) { ip = 0; ++ig; }
     };
     auto consume = [&](int slot) {
-        uint32_t xp[P];
-        {
-            const uint8_t *lx = lds + lds_lane + cp * 1024;
-            const uint4 a = *(const uint4 *)lx;
-            xp[0] = a.x; xp[1] = a.y; xp[2] = a.z; xp[3] = a.w;
-            if (TYPE == 0) xp[4] = *(const uint32_t *)(lds + 16 * nwp + lane * 4 + cp * 256);
-        }
+        float part[R];
+        uint32_t words[R][V], scale[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            half2_t t[P];
-            Unpack<TYPE>::run(qw[slot][r], t);
-            acc[r] = __builtin_fmaf(half_bits_to_float(qs[slot][r]), dot_pairs0(t, xp), acc[r]);
+            if constexpr (kSiw) {
+                const uint32_t d0 = qw[slot][r][0], d1 = qw[slot][r][V - 1], d2 = qs[slot][r];
+                words[r][0] = __builtin_amdgcn_perm(d1, d0, wsel);
+                words[r][V - 1] = __builtin_amdgcn_perm(d2, d1, wsel);
+                scale[r] = (uint32_t)__builtin_amdgcn_mov_dpp((int)d0, 0x00, 0xf, 0xf, false);  // quad_perm [0,0,0,0]
+            } else {
+#pragma unroll
+                for (int v = 0; v < V; ++v) words[r][v] = qw[slot][r][v];
+                scale[r] = qs[slot][r];
+            }
         }
-        if (++cp == nfull) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            uint32_t xp[P];
+            const u32x4 a = lds_a[v * per + cp * 64];
+            xp[0] = a[0]; xp[1] = a[1]; xp[2] = a[2]; xp[3] = a[3];
+            if constexpr (TYPE == 0) xp[P - 1] = lds_b[v * per + cp * 64];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                half2_t t[P];
+                Unpack<TYPE>::run(words[r][v], t);
+                part[r] = v == 0 ? dot_pairs0(t, xp) : dot_pairs(t, xp, part[r]);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = __builtin_fmaf(half_bits_to_float(scale[r]), part[r], acc[r]);
+        if (++cp == npass) {
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const float v = wave_sum(acc[r]);
@@ -212,16 +273,14 @@ __device__ __forceinline__ void stream_wave(const Prob &p, int row0, int nrows, 
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 }
 
-template <int R, int U>
-__global__ __launch_bounds__(kThreads) void gemv_stream(StreamArgs args, int rows_per_wave)
+template <int R, int U, int V>
+__global__ __launch_bounds__(kThreads) void gemv_stream(StreamArgs args)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int wave = uniform(threadIdx.x >> 6);
-    const int tile_rows = kWaves * rows_per_wave;
 
     int cur = -1;
     Prob p;
-    int nwp = 0;
     int tile_end = 0;
     for (int tile = blockIdx.x; tile < args.total_tiles; tile += gridDim.x) {
         if (tile >= tile_end || cur < 0) {
@@ -240,23 +299,23 @@ __global__ __launch_bounds__(kThreads) void gemv_stream(StreamArgs args, int row
                     p.nw = uniform(c.nw);
                     p.type = uniform(c.type);
                     p.tile0 = uniform(c.tile0);
+                    p.rpw = uniform(c.rpw);
                     tile_end = uniform(next0);
                     break;
                 }
                 ++i;
             }
             cur = i;
-            nwp = p.nw;
             __syncthreads();
-            stage_x(p, nwp, lds);
+            stage_x<V>(p, lds);
             __syncthreads();
         }
-        const int row0 = (tile - p.tile0) * tile_rows + wave * rows_per_wave;
+        const int row0 = ((tile - p.tile0) * kWaves + wave) * p.rpw;
         if (row0 < p.N) {
             if (p.type == 0)
-                stream_wave<0, R, U>(p, row0, rows_per_wave, nwp, lds);
+                stream_wave<0, R, U, V>(p, row0, p.rpw, lds);
             else
-                stream_wave<1, R, U>(p, row0, rows_per_wave, nwp, lds);
+                stream_wave<1, R, U, V>(p, row0, p.rpw, lds);
         }
     }
 }
@@ -419,12 +478,13 @@ __global__ __launch_bounds__(256) void dequant(const uint8_t *W, int64_t N, int6
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-constexpr int kR = 2;   // rows per group in gemv_stream
-constexpr int kU = 4;   // items (passes of 8 blocks x R rows) in flight per wave
+constexpr int kR = PN_ROWS_PER_GROUP;   // rows per group in gemv_stream
+constexpr int kU = PN_ITEMS_IN_FLIGHT;  // items (one pass of 8 blocks x R rows) in flight per wave
 
+// Per device: CU count and gemv_stream occupancy by LDS size (1 KiB steps).
 struct DeviceInfo {
     int cus = 0;
-    int occ[5] = {0, 0, 0, 0, 0};  // gemv_stream workgroups per CU, by LDS quarter (16 KB steps)
+    signed char occ[65];
 };
 
 DeviceInfo g_dev[64];
@@ -438,24 +498,26 @@ const DeviceInfo &device_info()
         int cus = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
-        for (int q = 0; q < 5; ++q) {
-            int occ = 0;
-            const size_t lds = (size_t)(q == 0 ? 1 : q * 16) * 1024;
-            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemv_stream<kR, kU>, kThreads, lds) !=
-                    hipSuccess ||
-                occ <= 0)
-                occ = 1;
-            d.occ[q] = occ;
-        }
+        memset(d.occ, 0, sizeof(d.occ));
         d.cus = cus;
     }
     return d;
 }
 
-int stream_wgs_per_cu(const DeviceInfo &d, int lds)
+int stream_wgs_per_cu(const DeviceInfo &dc, int lds)
 {
-    const int q = (lds + 16 * 1024 - 1) / (16 * 1024);
-    return d.occ[q < 0 ? 0 : (q > 4 ? 4 : q)];
+    DeviceInfo &d = const_cast<DeviceInfo &>(dc);
+    int q = (lds + 1023) / 1024;
+    q = q < 0 ? 0 : (q > 64 ? 64 : q);
+    if (d.occ[q] == 0) {
+        int occ = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemv_stream<kR, kU, 2>, kThreads,
+                                                         (size_t)q * 1024) != hipSuccess ||
+            occ <= 0)
+            occ = 1;
+        d.occ[q] = (signed char)(occ > 127 ? 127 : occ);
+    }
+    return d.occ[q];
 }
 
 bool type_ok(int t) { return t == PN_PN3T || t == PN_PN4T; }
@@ -482,40 +544,72 @@ Prob make_prob(int t, const void *W, int64_t N, int64_t K, const void *x, float 
     p.nw = (int32_t)(K / wpb(t) * 8);
     p.type = t;
     p.tile0 = 0;
+    p.rpw = kR;
     return p;
 }
 
 int lds_bytes_for(const Prob &p) { return p.type == 0 ? 20 * p.nw : 16 * p.nw; }
 
-// gemv_stream takes rows made of whole passes (8 blocks) whose activation
-// fits in LDS, and rows of at most 32 MiB.
+// gemv_stream takes rows made of whole passes of 8 blocks whose activation
+// fits in LDS; rows of whole 16-block passes use two words per lane.
 bool stream_ok(const Prob &p)
 {
     return (p.nw & 63) == 0 && lds_bytes_for(p) <= kMaxLdsBytes;
 }
+bool stream_v2(const Prob &p) { return (p.nw & 127) == 0; }
 
-// Rows per wave: enough waves to fill the device, at most 64 rows (one
-// result lane each), a multiple of kR.
-int rows_per_wave(int64_t total_rows, int lds)
+// Tiles: a wave-tile is `rpw` consecutive rows of one problem (at most 64:
+// one result lane each; a multiple of kR), a workgroup-tile is kWaves of
+// them, and workgroups take tiles in a grid stride.  Tiles are sized in
+// bytes, the same for every problem of a launch, so that the stride hands
+// every workgroup about the same amount of data: about 1/24 of a wave's
+// share of the launch, at least 16 KiB and at most 96 KiB per wave-tile.
+#ifndef PN_TILES_PER_WAVE
+#define PN_TILES_PER_WAVE 24
+#endif
+#ifndef PN_MAX_WAVE_TILE_KB
+#define PN_MAX_WAVE_TILE_KB 96
+#endif
+constexpr int64_t kTilesPerWave = PN_TILES_PER_WAVE;
+constexpr int64_t kMinWaveTileBytes = 16 * 1024;
+constexpr int64_t kMaxWaveTileBytes = PN_MAX_WAVE_TILE_KB * 1024;
+
+int64_t row_bytes_of(const Prob &p) { return (int64_t)(p.nw >> 3) * 34; }
+
+// Set rpw and tile0 of every problem; returns the number of tiles, or -1.
+int64_t plan_tiles(Prob *probs, int count, int lds)
 {
     const DeviceInfo &d = device_info();
     const int64_t waves = (int64_t)d.cus * stream_wgs_per_cu(d, lds) * kWaves;
-    int64_t rw = (total_rows + waves - 1) / waves;
-    rw = (rw + kR - 1) / kR * kR;
-    if (rw < kR) rw = kR;
-    if (rw > 64) rw = 64;
-    return (int)rw;
+    int64_t bytes = 0;
+    for (int i = 0; i < count; ++i) bytes += (int64_t)probs[i].N * row_bytes_of(probs[i]);
+    int64_t target = bytes / (waves * kTilesPerWave);
+    if (target < kMinWaveTileBytes) target = kMinWaveTileBytes;
+    if (target > kMaxWaveTileBytes) target = kMaxWaveTileBytes;
+    int64_t tiles = 0;
+    for (int i = 0; i < count; ++i) {
+        Prob &p = probs[i];
+        int64_t rpw = (target / row_bytes_of(p) + kR / 2) / kR * kR;
+        if (rpw < kR) rpw = kR;
+        if (rpw > 64) rpw = 64;
+        p.rpw = (int32_t)rpw;
+        p.tile0 = (int32_t)tiles;
+        tiles += ((int64_t)p.N + kWaves * rpw - 1) / (kWaves * rpw);
+        if (tiles > INT32_MAX) return -1;
+    }
+    return tiles;
 }
 
-int64_t tiles_of(const Prob &p, int rw) { return ((int64_t)p.N + kWaves * rw - 1) / (kWaves * rw); }
-
-pn_status launch_stream(StreamArgs &a, int lds, int rw, hipStream_t s, int variant)
+pn_status launch_stream(StreamArgs &a, int lds, bool v2, hipStream_t s, int variant)
 {
     const DeviceInfo &d = device_info();
     int grid = d.cus * stream_wgs_per_cu(d, lds);
     if (grid > a.total_tiles) grid = a.total_tiles;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((gemv_stream<kR, kU>), dim3(grid), dim3(kThreads), lds, s, a, rw);
+    if (v2)
+        hipLaunchKernelGGL((gemv_stream<kR, kU, 2>), dim3(grid), dim3(kThreads), lds, s, a);
+    else
+        hipLaunchKernelGGL((gemv_stream<kR, kU, 1>), dim3(grid), dim3(kThreads), lds, s, a);
     if (hipGetLastError() != hipSuccess) return PN_ELAUNCH;
     g_last_variant = variant;
     return PN_OK;
@@ -559,14 +653,15 @@ pn_status pn_gemv(pn_type t, const void *W, int64_t N, int64_t K, const void *x,
     hipStream_t s = (hipStream_t)stream;
     if (!stream_ok(p)) return launch_generic(p, p, 1, s);
     const int lds = lds_bytes_for(p);
-    const int rw = rows_per_wave(p.N, lds);
+    const int64_t tiles = plan_tiles(&p, 1, lds);
+    if (tiles < 0) return PN_EUNSUPPORTED;
     StreamArgs a;
     memset(&a, 0, sizeof(a));
     a.p0 = p;
     a.p1 = p;
     a.count = 1;
-    a.total_tiles = (int32_t)tiles_of(p, rw);
-    return launch_stream(a, lds, rw, s, kVarStream);
+    a.total_tiles = (int32_t)tiles;
+    return launch_stream(a, lds, stream_v2(p), s, kVarStream);
 }
 
 pn_status pn_gemv2(pn_type t, const void *W0, const void *W1, int64_t N, int64_t K, const void *x, float *y0,
@@ -583,15 +678,16 @@ pn_status pn_gemv2(pn_type t, const void *W0, const void *W1, int64_t N, int64_t
     hipStream_t s = (hipStream_t)stream;
     if (!stream_ok(p0)) return launch_generic(p0, p1, 2, s);
     const int lds = lds_bytes_for(p0);
-    const int rw = rows_per_wave(2 * (int64_t)p0.N, lds);
+    Prob pp[2] = {p0, p1};
+    const int64_t tiles = plan_tiles(pp, 2, lds);
+    if (tiles < 0) return PN_EUNSUPPORTED;
     StreamArgs a;
     memset(&a, 0, sizeof(a));
-    p1.tile0 = (int32_t)tiles_of(p0, rw);
-    a.p0 = p0;
-    a.p1 = p1;
+    a.p0 = pp[0];
+    a.p1 = pp[1];
     a.count = 2;
-    a.total_tiles = p1.tile0 + (int32_t)tiles_of(p1, rw);
-    return launch_stream(a, lds, rw, s, kVarStream);
+    a.total_tiles = (int32_t)tiles;
+    return launch_stream(a, lds, stream_v2(p0), s, kVarStream);
 }
 
 pn_status pn_gemm_smallm(pn_type t, const void *W, int64_t N, int64_t K, const void *X, int64_t ldx, int M,
@@ -644,7 +740,7 @@ struct pn_group {
     int count;
     int total_tiles;
     int lds;
-    int rows_per_wave;
+    bool v2;
 };
 
 pn_status pn_group_create(const pn_gemv_desc *descs, int count, pn_group **out)
@@ -654,7 +750,7 @@ pn_status pn_group_create(const pn_gemv_desc *descs, int count, pn_group **out)
     Prob *host = (Prob *)calloc((size_t)count, sizeof(Prob));
     if (!host) return PN_ENOMEM;
     int lds = 0;
-    int64_t rows = 0;
+    bool v2 = true;
     pn_status st = PN_OK;
     for (int i = 0; i < count && st == PN_OK; ++i) {
         const pn_gemv_desc &e = descs[i];
@@ -666,17 +762,12 @@ pn_status pn_group_create(const pn_gemv_desc *descs, int count, pn_group **out)
             if (!stream_ok(host[i])) st = PN_EUNSUPPORTED;
         }
         if (st == PN_OK) {
-            rows += host[i].N;
+            v2 = v2 && stream_v2(host[i]);
             if (lds_bytes_for(host[i]) > lds) lds = lds_bytes_for(host[i]);
         }
     }
-    const int rw = st == PN_OK ? rows_per_wave(rows, lds) : 0;
-    int64_t tiles = 0;
-    for (int i = 0; i < count && st == PN_OK; ++i) {
-        host[i].tile0 = (int32_t)tiles;
-        tiles += tiles_of(host[i], rw);
-        if (tiles > INT32_MAX) st = PN_EUNSUPPORTED;
-    }
+    const int64_t tiles = st == PN_OK ? plan_tiles(host, count, lds) : 0;
+    if (tiles < 0) st = PN_EUNSUPPORTED;
     if (st != PN_OK) {
         free(host);
         return st;
@@ -701,7 +792,7 @@ pn_status pn_group_create(const pn_gemv_desc *descs, int count, pn_group **out)
     g->count = count;
     g->total_tiles = (int)tiles;
     g->lds = lds;
-    g->rows_per_wave = rw;
+    g->v2 = v2;
     *out = g;
     return PN_OK;
 }
@@ -714,7 +805,7 @@ pn_status pn_group_run(const pn_group *g, void *stream)
     a.table = g->table;
     a.count = g->count;
     a.total_tiles = g->total_tiles;
-    return launch_stream(a, g->lds, g->rows_per_wave, (hipStream_t)stream, kVarGroupStream);
+    return launch_stream(a, g->lds, g->v2, (hipStream_t)stream, kVarGroupStream);
 }
 
 void pn_group_destroy(pn_group *g)
