@@ -188,6 +188,23 @@ def main():
     del sw
     torch.cuda.empty_cache()
 
+    # read ceiling of the device, measured with the library's streaming-read probe
+    buf = torch.zeros(8 << 30, dtype=torch.uint8, device="cuda")
+    scratch = torch.empty(B.pn_read_probe_scratch_bytes() // 4, dtype=torch.int32, device="cuda")
+    best = None
+    for _ in range(6):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        nread = B.pn_read_probe(buf, buf.numel(), scratch, scratch.numel() * 4)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None or ms < best else best
+    read_ceiling = nread / (best * 1e-3) / 1e9
+    del buf, scratch
+    torch.cuda.empty_cache()
+    log("read ceiling %.1f GB/s" % read_ceiling)
+
     cpu = None
     if not args.no_cpu_baseline and m is None:
         log("cpu baseline: oracle on %d layers, %d threads" % (args.cpu_layers, threads))
@@ -219,6 +236,8 @@ def main():
                    "launches_per_token": launches},
         "tokens_per_s": round(tok_s, 2),
         "frac_of_peak": round(value / PEAK_GBPS, 4),
+        "read_ceiling_gbps": round(read_ceiling, 1),
+        "frac_of_read_ceiling": round(value / read_ceiling, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "other_schedules": secondary,

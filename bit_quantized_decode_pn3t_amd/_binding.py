@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpn.so")
 # Every symbol include/pn.h declares.
 EXPORTS = ("pn_weights_per_block", "pn_row_bytes", "pn_gemv", "pn_gemv2",
            "pn_gemm_smallm", "pn_dequantize", "pn_group_create", "pn_group_run",
-           "pn_group_destroy", "pn_status_str", "pn_last_variant", "pn_variant_name")
+           "pn_group_destroy", "pn_read_probe_scratch_bytes", "pn_read_probe", "pn_status_str",
+           "pn_last_variant", "pn_variant_name")
 
 
 class PNError(RuntimeError):
@@ -70,6 +71,10 @@ def lib():
     L.pn_group_run.restype = i32
     L.pn_group_destroy.argtypes = [vp]
     L.pn_group_destroy.restype = None
+    L.pn_read_probe_scratch_bytes.argtypes = []
+    L.pn_read_probe_scratch_bytes.restype = ctypes.c_size_t
+    L.pn_read_probe.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t), vp]
+    L.pn_read_probe.restype = i32
     L.pn_status_str.argtypes = [i32]
     L.pn_status_str.restype = ctypes.c_char_p
     L.pn_last_variant.argtypes = []
@@ -177,6 +182,20 @@ class Group:
 
 def pn_group_create(problems):
     return Group(problems)
+
+
+def pn_read_probe_scratch_bytes():
+    return lib().pn_read_probe_scratch_bytes()
+
+
+def pn_read_probe(buf, nbytes, scratch, scratch_bytes, stream=None, check=True):
+    """Launch the streaming-read probe; returns the number of bytes it reads."""
+    got = ctypes.c_size_t(0)
+    st = lib().pn_read_probe(_ptr(buf), nbytes, _ptr(scratch), scratch_bytes, ctypes.byref(got),
+                             _stream(stream))
+    if check:
+        _check(st, "pn_read_probe")
+    return got.value
 
 
 def pn_last_variant():

@@ -273,39 +273,47 @@ __device__ __forceinline__ void stream_wave(const Prob &p, int row0, int nrows, 
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 }
 
+// Problem i of a launch (inline for one or two problems, else the table).
+__device__ __forceinline__ const Prob *problem(const StreamArgs &a, int i)
+{
+    if (a.table) return a.table + i;
+    return i == 0 ? &a.p0 : &a.p1;
+}
+
+__device__ __forceinline__ int problem_tile0(const StreamArgs &a, int i)
+{
+    if (i >= a.count) return a.total_tiles;
+    if (a.table) return a.table[i].tile0;
+    return i == 0 ? a.p0.tile0 : a.p1.tile0;
+}
+
+// Workgroups take tiles in a grid stride: at any moment the workgroups work on
+// neighbouring tiles, i.e. one contiguous stretch of the weights, which the
+// memory system serves better than scattered streams.  A workgroup stages
+// the activation into LDS whenever its next tile belongs to another problem.
 template <int R, int U, int V>
 __global__ __launch_bounds__(kThreads) void gemv_stream(StreamArgs args)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int wave = uniform(threadIdx.x >> 6);
-
-    int cur = -1;
+    int i = 0;
+    int next0 = -1;  // first tile of problem i + 1; -1 before the first problem
     Prob p;
-    int tile_end = 0;
     for (int tile = blockIdx.x; tile < args.total_tiles; tile += gridDim.x) {
-        if (tile >= tile_end || cur < 0) {
-            // Find the problem holding this tile (tiles only move forward).
-            int i = cur < 0 ? 0 : cur;
-            for (;;) {
-                Prob c = args.table ? args.table[i] : (i == 0 ? args.p0 : args.p1);
-                int next0 = (i + 1 < args.count)
-                                ? (args.table ? args.table[i + 1].tile0 : args.p1.tile0)
-                                : args.total_tiles;
-                if (tile < next0) {
-                    p.W = uniform_ptr(c.W);
-                    p.x = uniform_ptr(c.x);
-                    p.y = uniform_ptr(c.y);
-                    p.N = uniform(c.N);
-                    p.nw = uniform(c.nw);
-                    p.type = uniform(c.type);
-                    p.tile0 = uniform(c.tile0);
-                    p.rpw = uniform(c.rpw);
-                    tile_end = uniform(next0);
-                    break;
-                }
-                ++i;
-            }
-            cur = i;
+        if (tile >= next0) {
+            // advance to the problem holding this tile (tiles only move forward)
+            if (next0 >= 0) ++i;
+            while (problem_tile0(args, i + 1) <= tile) ++i;
+            const Prob &c = *problem(args, i);
+            p.W = uniform_ptr(c.W);
+            p.x = uniform_ptr(c.x);
+            p.y = uniform_ptr(c.y);
+            p.N = uniform(c.N);
+            p.nw = uniform(c.nw);
+            p.type = uniform(c.type);
+            p.tile0 = uniform(c.tile0);
+            p.rpw = uniform(c.rpw);
+            next0 = uniform(problem_tile0(args, i + 1));
             __syncthreads();
             stage_x<V>(p, lds);
             __syncthreads();
@@ -571,7 +579,10 @@ bool stream_v2(const Prob &p) { return (p.nw & 127) == 0; }
 #define PN_MAX_WAVE_TILE_KB 96
 #endif
 constexpr int64_t kTilesPerWave = PN_TILES_PER_WAVE;
-constexpr int64_t kMinWaveTileBytes = 16 * 1024;
+#ifndef PN_MIN_WAVE_TILE_KB
+#define PN_MIN_WAVE_TILE_KB 16
+#endif
+constexpr int64_t kMinWaveTileBytes = PN_MIN_WAVE_TILE_KB * 1024;
 constexpr int64_t kMaxWaveTileBytes = PN_MAX_WAVE_TILE_KB * 1024;
 
 int64_t row_bytes_of(const Prob &p) { return (int64_t)(p.nw >> 3) * 34; }

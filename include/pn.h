@@ -127,6 +127,20 @@ pn_status pn_group_run(const pn_group *g, void *stream);
 /* Free a plan (NULL is allowed).  Synchronises the device first. */
 void pn_group_destroy(pn_group *g);
 
+/* Streaming-read probe: the practical HBM read ceiling of the device,
+ * measured in the same harness as the GEMV (the v100-skinny README, "Kernel
+ * benchmarks", rates its kernels against a measured read-only ceiling).  One
+ * launch reads `*bytes_read` bytes (the largest multiple of the launch's
+ * granule not above `bytes`, at least 1 KiB per wave) from `buf` with
+ * coalesced 16-byte nontemporal loads and writes a checksum word per lane to
+ * `scratch`.
+ *   buf     : device, 16-byte aligned, `bytes` readable
+ *   scratch : device, 4-byte aligned, pn_read_probe_scratch_bytes() bytes
+ * Returns PN_ESHAPE if `bytes` is too small or `scratch_bytes` too small. */
+size_t pn_read_probe_scratch_bytes(void);
+pn_status pn_read_probe(const void *buf, size_t bytes, void *scratch, size_t scratch_bytes,
+                        size_t *bytes_read, void *stream);
+
 /* Text for a status code. */
 const char *pn_status_str(pn_status e);
 

@@ -254,3 +254,19 @@ def test_gemm_smallm(t, n, k, m):
         y1 = gpu_gemv(t, w, n, k, X[0, :k])
         # both within TOL of the fp64 sum, so within 2 * TOL of each other
         assert_gemv_close(Y[0, :n], y1.astype(np.float64), a[0], "smallm vs gemv", tol=2 * TOL)
+
+
+def test_read_probe():
+    """The streaming-read probe reads what it reports and folds it exactly:
+    the XOR of all per-lane checksums equals the XOR of every word read."""
+    say("read probe")
+    n = 64 << 20
+    rs = np.random.default_rng(9)
+    host = rs.integers(0, 2 ** 32, size=n // 4, dtype=np.uint32)
+    buf = dev(host.view(np.uint8))
+    scratch = torch.zeros(B.pn_read_probe_scratch_bytes() // 4, dtype=torch.int32, device="cuda")
+    got = B.pn_read_probe(buf, n, scratch, scratch.numel() * 4)
+    sync()
+    assert 0 < got <= n and got % 1024 == 0
+    want = np.bitwise_xor.reduce(host[: got // 4])
+    assert np.bitwise_xor.reduce(scratch.cpu().numpy().view(np.uint32)) == want
