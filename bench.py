@@ -7,7 +7,11 @@ A step is one token: every one of the 448 GEMVs, each with its own fp16
 input, all inputs resident in HBM before timing starts.  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--schedule token|layer|gemv]
-                  [--config 3|4] [--no-cpu-baseline]
+                  [--config 3|4] [--math mfma|valu] [--no-cpu-baseline]
+
+--config 4 runs the same sweep with M = 8 activation rows per matrix (the
+small-batch kernels; --math picks their arithmetic, the other one is timed
+beside it).
 
 value = algorithmic bytes per token (packed weights + fp16 inputs + fp32
 outputs) / step time, in GB/s; tokens/s is reported beside it.
@@ -55,19 +59,23 @@ def measured_traffic(workload):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(layers, threads):
+def cpu_baseline(layers, threads, m=None):
     """The oracle (fp64 decode + GEMV, C, OpenMP over rows) on a bounded
     sample of the sweep: the first `layers` layers, scaled to one token."""
     from bit_quantized_decode_pn3t_amd import synth
     from oracle import pnref
 
     used = pnref.set_threads(threads)
-    recs = synth.sweep_matrices(layers=layers, threads=threads)
+    recs = synth.sweep_matrices(layers=layers, m=m, config=3 if m is None else 4, threads=threads)
     sample_bytes = sum(r["W"].nbytes for r in recs)
-    pnref.gemv_f64(recs[0]["type"], recs[0]["W"][:64], 64, recs[0]["K"], recs[0]["x"])  # warm
+    pnref.gemv_f64(recs[0]["type"], recs[0]["W"][:64], 64, recs[0]["K"],
+                   recs[0]["x"] if m is None else recs[0]["x"][0])  # warm
     t0 = time.perf_counter()
     for r in recs:
-        pnref.gemv_f64(r["type"], r["W"], r["N"], r["K"], r["x"])
+        if m is None:
+            pnref.gemv_f64(r["type"], r["W"], r["N"], r["K"], r["x"])
+        else:
+            pnref.gemm_f64(r["type"], r["W"], r["N"], r["K"], r["x"])
     dt = time.perf_counter() - t0
     return dt, sample_bytes, used
 
@@ -79,10 +87,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--schedule", default="token", choices=["token", "layer", "gemv"])
     ap.add_argument("--config", type=int, default=3, choices=[3, 4])
+    ap.add_argument("--math", default="mfma", choices=["mfma", "valu"],
+                    help="small-batch arithmetic (--config 4)")
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the other schedules")
-    ap.add_argument("--cpu-layers", type=int, default=64)
+    ap.add_argument("--cpu-layers", type=int, default=None,
+                    help="layers in the oracle's sample (default 64 at M=1, 8 at M=8)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run one device copy of this many MiB (a kernel of known traffic "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -110,7 +121,12 @@ def main():
         log("copy calibration: %d bytes read, %d written" % (n, n))
         del src, dst
     m = None if args.config == 3 else 8
-    schedule = args.schedule if m is None else "gemv"
+    schedule = args.schedule
+    if m is not None and schedule == "layer":
+        print("--config 4 runs the token and gemv schedules", file=sys.stderr)
+        sys.exit(2)
+    if m is not None:
+        B.pn_set_smallm_math(args.math)
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
 
     t0 = time.perf_counter()
@@ -159,14 +175,15 @@ def main():
     value = bytes_per_token / (wall / args.steps) / 1e9
     tok_s = args.steps / wall
 
-    workload = "sweep64_m%d_%s" % (m or 1, schedule)
+    workload = "sweep64_m1_%s" % schedule if m is None else "sweep64_m%d_%s_%s" % (m, schedule, args.math)
     if schedule == "token":
         # one launch per step: the events bracket exactly the dominant kernel
         kern_ms = sum(ev_ms) / len(ev_ms)
         achieved = bytes_per_token / (kern_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / PEAK_GBPS, 4), "traffic": measured_traffic(workload),
-                    "kernel": "gemv_stream", "kernel_avg_ms": round(kern_ms, 4),
+                    "kernel": "gemv_stream" if m is None else "gemm_stream<%s>" % args.math,
+                    "variant": variant, "kernel_avg_ms": round(kern_ms, 4),
                     "algorithmic_bytes_per_launch": bytes_per_token}
     else:
         roofline = {"bound": "hbm", "achieved": round(value, 1), "peak": PEAK_GBPS, "unit": "GB/s",
@@ -175,15 +192,24 @@ def main():
 
     launches = sw.launches(schedule)
     secondary = {}
-    if not args.no_secondary and m is None:
-        for other in ("layer", "gemv"):
-            if other == schedule:
-                continue
-            w2, _, _ = run_timed(other, args.steps, 2, False)
-            secondary[other] = {"tokens_per_s": round(args.steps / w2, 2),
-                                "gbps": round(bytes_per_token / (w2 / args.steps) / 1e9, 1),
-                                "launches_per_token": sw.launches(other)}
-            log("schedule %s: %.1f tok/s" % (other, args.steps / w2))
+    if not args.no_secondary:
+        if m is None:
+            others = [(o, None) for o in ("layer", "gemv") if o != schedule]
+        else:
+            other_math = "valu" if args.math == "mfma" else "mfma"
+            others = [(o, args.math) for o in ("token", "gemv") if o != schedule] + [(schedule, other_math)]
+        for other, math in others:
+            if math is not None:
+                B.pn_set_smallm_math(math)
+                sw.close()  # plans keep the arithmetic they were created with
+            w2, _, var2 = run_timed(other, args.steps, 2, False)
+            key = other if math is None else "%s_%s" % (other, math)
+            secondary[key] = {"tokens_per_s": round(args.steps / w2, 2),
+                              "gbps": round(bytes_per_token / (w2 / args.steps) / 1e9, 1),
+                              "launches_per_token": sw.launches(other), "variant": var2}
+            log("schedule %s: %.1f tok/s" % (key, args.steps / w2))
+        if m is not None:
+            B.pn_set_smallm_math(args.math)
     sw.close()
     del sw
     torch.cuda.empty_cache()
@@ -206,15 +232,17 @@ def main():
     log("read ceiling %.1f GB/s" % read_ceiling)
 
     cpu = None
-    if not args.no_cpu_baseline and m is None:
-        log("cpu baseline: oracle on %d layers, %d threads" % (args.cpu_layers, threads))
-        dt, sample_bytes, used = cpu_baseline(args.cpu_layers, threads)
+    if not args.no_cpu_baseline:
+        cpu_layers = args.cpu_layers or (64 if m is None else 8)
+        log("cpu baseline: oracle on %d layers, %d threads" % (cpu_layers, threads))
+        dt, sample_bytes, used = cpu_baseline(cpu_layers, threads, m)
         weights_per_token = sum(synth.row_bytes(t, k) * n for _, t, n, k in synth.SWEEP_LAYER) * args.layers
         token_fraction = sample_bytes / weights_per_token
         cpu = {"value": round(token_fraction / dt, 4), "unit": "tok/s", "cores": used, "kind": "oracle",
                "sample": "first %d of %d layers (%.2f GB packed, %.1f%% of a token) in %.2f s; "
-                         "fp64 decode+GEMV, OpenMP over rows" % (args.cpu_layers, args.layers,
-                                                                sample_bytes / 1e9, 100 * token_fraction, dt),
+                         "fp64 decode+%s, OpenMP over rows" % (cpu_layers, args.layers, sample_bytes / 1e9,
+                                                              100 * token_fraction, dt,
+                                                              "GEMV" if m is None else "GEMM (M=8)"),
                "gbps_packed": round(sample_bytes / dt / 1e9, 3)}
 
     out = {
@@ -230,7 +258,8 @@ def main():
         "vs_baseline": None,
         "dtype": "pn3t/pn4t weights, fp16 activations, fp32 accumulate",
         "data": "synthetic (seeded random codes and fp16 scales; fp16 N(0,1) activations)",
-        "config": {"workload": "64-layer 27B-shaped sweep, M=%d, %s schedule" % (m or 1, schedule),
+        "config": {"workload": "64-layer 27B-shaped sweep, M=%d, %s schedule%s" % (
+                       m or 1, schedule, "" if m is None else ", %s arithmetic" % args.math),
                    "layers": args.layers, "gemvs_per_token": 7 * args.layers,
                    "bytes_per_token": bytes_per_token, "schedule": schedule,
                    "launches_per_token": launches},

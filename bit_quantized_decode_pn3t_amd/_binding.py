@@ -15,6 +15,8 @@ PN_PN3T = 0
 PN_PN4T = 1
 TYPES = {"pn3t": PN_PN3T, "pn4t": PN_PN4T, PN_PN3T: PN_PN3T, PN_PN4T: PN_PN4T}
 
+SMALLM_MATH = {"mfma": 0, "valu": 1, 0: 0, 1: 1}
+
 STATUS = {0: "PN_OK", -1: "PN_EINVAL", -2: "PN_ESHAPE", -3: "PN_EALIGN",
           -4: "PN_EUNSUPPORTED", -5: "PN_ELAUNCH", -6: "PN_ENOMEM"}
 
@@ -22,9 +24,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpn.so")
 
 # Every symbol include/pn.h declares.
 EXPORTS = ("pn_weights_per_block", "pn_row_bytes", "pn_gemv", "pn_gemv2",
-           "pn_gemm_smallm", "pn_dequantize", "pn_group_create", "pn_group_run",
-           "pn_group_destroy", "pn_read_probe_scratch_bytes", "pn_read_probe", "pn_status_str",
-           "pn_last_variant", "pn_variant_name")
+           "pn_gemm_smallm", "pn_set_smallm_math", "pn_get_smallm_math", "pn_dequantize",
+           "pn_group_create", "pn_group_create_smallm", "pn_group_run", "pn_group_destroy",
+           "pn_read_probe_scratch_bytes", "pn_read_probe", "pn_status_str", "pn_last_variant",
+           "pn_variant_name")
 
 
 class PNError(RuntimeError):
@@ -38,6 +41,12 @@ class pn_gemv_desc(ctypes.Structure):
     _fields_ = [("W", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
                 ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("type", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)]
+
+
+class pn_gemm_desc(ctypes.Structure):
+    _fields_ = [("W", ctypes.c_void_p), ("X", ctypes.c_void_p), ("Y", ctypes.c_void_p),
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("ldx", ctypes.c_int64),
+                ("ldy", ctypes.c_int64), ("type", ctypes.c_int32), ("M", ctypes.c_int32)]
 
 
 _lib = None
@@ -63,6 +72,12 @@ def lib():
     L.pn_gemv2.restype = i32
     L.pn_gemm_smallm.argtypes = [i32, vp, i64, i64, vp, i64, i32, vp, i64, vp]
     L.pn_gemm_smallm.restype = i32
+    L.pn_set_smallm_math.argtypes = [i32]
+    L.pn_set_smallm_math.restype = i32
+    L.pn_get_smallm_math.argtypes = []
+    L.pn_get_smallm_math.restype = i32
+    L.pn_group_create_smallm.argtypes = [ctypes.POINTER(pn_gemm_desc), i32, ctypes.POINTER(vp)]
+    L.pn_group_create_smallm.restype = i32
     L.pn_dequantize.argtypes = [i32, vp, i64, i64, vp, vp]
     L.pn_dequantize.restype = i32
     L.pn_group_create.argtypes = [ctypes.POINTER(pn_gemv_desc), i32, ctypes.POINTER(vp)]
@@ -146,6 +161,18 @@ def pn_gemm_smallm(pn_type, W, N, K, X, ldx, M, Y, ldy, stream=None, check=True)
     return st
 
 
+def pn_set_smallm_math(math, check=True):
+    """Select the small-M arithmetic: "mfma" (default) or "valu"."""
+    st = lib().pn_set_smallm_math(SMALLM_MATH.get(math, math if isinstance(math, int) else -1))
+    if check:
+        _check(st, "pn_set_smallm_math")
+    return st
+
+
+def pn_get_smallm_math():
+    return {0: "mfma", 1: "valu"}[lib().pn_get_smallm_math()]
+
+
 def pn_dequantize(pn_type, W, N, K, out, stream=None, check=True):
     st = lib().pn_dequantize(_t(pn_type), _ptr(W), N, K, _ptr(out), _stream(stream))
     if check:
@@ -154,14 +181,23 @@ def pn_dequantize(pn_type, W, N, K, out, stream=None, check=True):
 
 
 class Group:
-    """A pn_group plan over (pn_type, W, N, K, x, y) problems; frees itself."""
+    """A pn_group plan over (pn_type, W, N, K, x, y) problems; frees itself.
+    With smallm=True the problems are (pn_type, W, N, K, X, ldx, M, Y, ldy)
+    and the plan comes from pn_group_create_smallm."""
 
-    def __init__(self, problems):
-        arr = (pn_gemv_desc * len(problems))()
-        for i, (t, W, N, K, x, y) in enumerate(problems):
-            arr[i] = pn_gemv_desc(_ptr(W), _ptr(x), _ptr(y), N, K, _t(t), 0)
+    def __init__(self, problems, smallm=False):
         h = ctypes.c_void_p()
-        _check(lib().pn_group_create(arr, len(problems), ctypes.byref(h)), "pn_group_create")
+        if smallm:
+            arr = (pn_gemm_desc * len(problems))()
+            for i, (t, W, N, K, X, ldx, M, Y, ldy) in enumerate(problems):
+                arr[i] = pn_gemm_desc(_ptr(W), _ptr(X), _ptr(Y), N, K, ldx, ldy, _t(t), M)
+            _check(lib().pn_group_create_smallm(arr, len(problems), ctypes.byref(h)),
+                   "pn_group_create_smallm")
+        else:
+            arr = (pn_gemv_desc * len(problems))()
+            for i, (t, W, N, K, x, y) in enumerate(problems):
+                arr[i] = pn_gemv_desc(_ptr(W), _ptr(x), _ptr(y), N, K, _t(t), 0)
+            _check(lib().pn_group_create(arr, len(problems), ctypes.byref(h)), "pn_group_create")
         self.handle = h
         self.keep = problems  # the plan holds raw device pointers
 
@@ -182,6 +218,10 @@ class Group:
 
 def pn_group_create(problems):
     return Group(problems)
+
+
+def pn_group_create_smallm(problems):
+    return Group(problems, smallm=True)
 
 
 def pn_read_probe_scratch_bytes():

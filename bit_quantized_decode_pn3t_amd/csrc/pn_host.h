@@ -1,0 +1,66 @@
+// pn_host.h - host-side helpers shared by the library's sources (argument
+// checks, device facts, the kernel-variant census and the group plan).
+// Internal to libpn.so; the public interface is include/pn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pn.h"
+
+namespace pn {
+namespace host {
+
+// Kernel variants, as reported by pn_last_variant / pn_variant_name.
+enum Variant {
+    kVarNone = 0,
+    kVarStream = 1,
+    kVarGeneric = 2,
+    kVarSmallMValu = 3,
+    kVarDequant = 4,
+    kVarGroupStream = 5,
+    kVarSmallMMfma = 6,
+    kVarGroupSmallMValu = 7,
+    kVarGroupSmallMMfma = 8,
+};
+
+extern thread_local int g_last_variant;
+
+inline bool type_ok(int t) { return t == PN_PN3T || t == PN_PN4T; }
+inline int wpb(int t) { return t == PN_PN3T ? 80 : 64; }
+inline bool aligned4(const void *p) { return ((uintptr_t)p & 3) == 0; }
+
+// Checks shared by every entry point that takes a packed matrix.
+inline pn_status check_matrix(int t, const void *W, int64_t N, int64_t K)
+{
+    if (!type_ok(t) || !W) return PN_EINVAL;
+    if (N < 1 || K < wpb(t) || K % wpb(t) != 0) return PN_ESHAPE;
+    if ((uintptr_t)W & 1) return PN_EALIGN;
+    if (N > INT32_MAX || K / wpb(t) * 34 > INT32_MAX) return PN_EUNSUPPORTED;
+    return PN_OK;
+}
+
+// Compute units of the current device (256 if the query fails).
+int device_cus();
+
+enum GroupKind { kGroupGemv = 0, kGroupSmallM = 1 };
+
+}  // namespace host
+}  // namespace pn
+
+// A launch plan built by pn_group_create / pn_group_create_smallm.
+struct pn_group {
+    int kind;           // pn::host::GroupKind
+    void *table;        // device copy of the per-problem records
+    int count;
+    int total_tiles;
+    int lds;            // dynamic LDS bytes of the launch
+    int flags;          // kind-specific launch choice
+};
+
+namespace pn {
+namespace host {
+// Launch a small-M group plan (pn_smallm.hip).
+pn_status smallm_group_run(const pn_group *g, hipStream_t s);
+}  // namespace host
+}  // namespace pn

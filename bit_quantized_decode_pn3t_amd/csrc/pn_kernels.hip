@@ -13,18 +13,20 @@
 //                 word"), so one LDS read of x serves R rows.
 //   gemv_generic  M = 1 fallback for shapes gemv_stream does not take (x too
 //                 large for LDS): one wave per row, x from global memory.
-//   gemm_smallm   M <= 8: x chunks for all M rows staged in LDS, each weight
-//                 decoded once and used M times.
 //   dequant       dense fp32 weights, bit-exact.
+// The small-batch (M <= 8) kernels are in pn_smallm.hip.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 #include "pn_device.h"
-#include "../../include/pn.h"
+#include "pn_host.h"
 
 using namespace pn;
+using namespace pn::host;
+
+thread_local int pn::host::g_last_variant = pn::host::kVarNone;
 
 namespace {
 
@@ -53,17 +55,6 @@ namespace {
 constexpr int kWaves = PN_WAVES;        // waves per workgroup
 constexpr int kThreads = 64 * kWaves;   // workgroup size
 constexpr int kMaxLdsBytes = 64 * 1024; // LDS the streaming kernels may use
-
-enum Variant {
-    kVarNone = 0,
-    kVarStream = 1,
-    kVarGeneric = 2,
-    kVarSmallM = 3,
-    kVarDequant = 4,
-    kVarGroupStream = 5,
-};
-
-thread_local int g_last_variant = kVarNone;
 
 // One GEMV problem as the device sees it.
 struct Prob {
@@ -356,108 +347,6 @@ __global__ __launch_bounds__(kThreads) void gemv_generic(Prob p0, Prob p1)
 }
 
 // ---------------------------------------------------------------------------
-// Small M (1..8).  A workgroup owns kWaves * R rows; K is walked in chunks of
-// kChunkWords code words; each chunk's activations for all M rows are staged
-// in LDS (same split layout as stage_x).  A lane decodes its word once per
-// row and feeds M dot products.
-// ---------------------------------------------------------------------------
-constexpr int kChunkWords = 256;
-
-template <int TYPE, int MMAX, int R>
-__global__ __launch_bounds__(kThreads) void gemm_smallm(const uint8_t *W, int N, int nw,
-                                                        const uint8_t *X, int64_t ldx_bytes, int M,
-                                                        float *Y, int64_t ldy)
-{
-    constexpr int P = Unpack<TYPE>::kPairs;
-    constexpr int C = Fmt<TYPE>::C;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[MMAX * kChunkWords * C * 2];
-    const int lane = threadIdx.x & 63;
-    const int wave = uniform(threadIdx.x >> 6);
-    const uint32_t row_bytes = (uint32_t)(nw >> 3) * 34u;
-    const int tiles = (N + kWaves * R - 1) / (kWaves * R);
-
-    for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
-        const int row0 = tile * kWaves * R + wave * R;
-        const uint8_t *rowp[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            int rr = row0 + r < N ? row0 + r : N - 1;
-            rowp[r] = uniform_ptr(W + (size_t)rr * row_bytes);
-        }
-        float acc[R][MMAX];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int m = 0; m < MMAX; ++m) acc[r][m] = 0.0f;
-
-        for (int c0 = 0; c0 < nw; c0 += kChunkWords) {
-            const int cw = nw - c0 < kChunkWords ? nw - c0 : kChunkWords;
-            __syncthreads();
-            // stage X[:, C*c0 .. C*(c0+cw)) ; per m a region of kChunkWords*C*2 bytes
-            for (int i = threadIdx.x; i < M * kChunkWords; i += kThreads) {
-                const int m = i / kChunkWords, f = i % kChunkWords;
-                uint8_t *base = lds + (size_t)m * kChunkWords * C * 2;
-                if (TYPE == 0) {
-                    uint4 va = make_uint4(0, 0, 0, 0);
-                    uint32_t vb = 0;
-                    if (f < cw) {
-                        const uint8_t *src = X + m * ldx_bytes + (size_t)(c0 + f) * 20;
-                        va = make_uint4(load_u32(src), load_u32(src + 4), load_u32(src + 8), load_u32(src + 12));
-                        vb = load_u32(src + 16);
-                    }
-                    ((uint4 *)base)[f] = va;
-                    ((uint32_t *)(base + 16 * kChunkWords))[f] = vb;
-                } else {
-                    uint4 va = make_uint4(0, 0, 0, 0);
-                    if (f < cw) {
-                        const uint8_t *src = X + m * ldx_bytes + (size_t)(c0 + f) * 16;
-                        va = make_uint4(load_u32(src), load_u32(src + 4), load_u32(src + 8), load_u32(src + 12));
-                    }
-                    ((uint4 *)base)[f] = va;
-                }
-            }
-            __syncthreads();
-            if (row0 < N) {
-                for (int fl = lane; fl < cw; fl += 64) {
-                    const uint32_t f = (uint32_t)(c0 + fl);
-                    half2_t t[R][P];
-                    float d[R];
-#pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        Unpack<TYPE>::run(load_u32_a2(rowp[r] + word_off(f)), t[r]);
-                        d[r] = half_bits_to_float(load_u16(rowp[r] + scale_off(f)));
-                    }
-#pragma unroll
-                    for (int m = 0; m < MMAX; ++m) {
-                        if (m < M) {
-                            const uint8_t *base = lds + (size_t)m * kChunkWords * C * 2;
-                            uint32_t xp[P];
-                            const uint4 a = ((const uint4 *)base)[fl];
-                            xp[0] = a.x; xp[1] = a.y; xp[2] = a.z; xp[3] = a.w;
-                            if (TYPE == 0) xp[P - 1] = ((const uint32_t *)(base + 16 * kChunkWords))[fl];
-#pragma unroll
-                            for (int r = 0; r < R; ++r)
-                                acc[r][m] = __builtin_fmaf(d[r], dot_pairs(t[r], xp, 0.0f), acc[r][m]);
-                        }
-                    }
-                }
-            }
-        }
-        if (row0 < N) {
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int m = 0; m < MMAX; ++m) {
-                    if (m < M) {
-                        const float v = wave_sum(acc[r][m]);
-                        if (lane == 0 && row0 + r < N) Y[(int64_t)m * ldy + row0 + r] = v;
-                    }
-                }
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
 // Dequantization: one thread per code word, C fp32 outputs each.
 // out = d * (float)(n - z): one binary32 multiply of two exact values.
 // ---------------------------------------------------------------------------
@@ -512,6 +401,12 @@ const DeviceInfo &device_info()
     return d;
 }
 
+}  // namespace
+
+int pn::host::device_cus() { return device_info().cus; }
+
+namespace {
+
 int stream_wgs_per_cu(const DeviceInfo &dc, int lds)
 {
     DeviceInfo &d = const_cast<DeviceInfo &>(dc);
@@ -527,20 +422,6 @@ int stream_wgs_per_cu(const DeviceInfo &dc, int lds)
     }
     return d.occ[q];
 }
-
-bool type_ok(int t) { return t == PN_PN3T || t == PN_PN4T; }
-int wpb(int t) { return t == PN_PN3T ? 80 : 64; }
-
-pn_status check_matrix(int t, const void *W, int64_t N, int64_t K)
-{
-    if (!type_ok(t) || !W) return PN_EINVAL;
-    if (N < 1 || K < wpb(t) || K % wpb(t) != 0) return PN_ESHAPE;
-    if ((uintptr_t)W & 1) return PN_EALIGN;
-    if (N > INT32_MAX || K / wpb(t) * 34 > INT32_MAX) return PN_EUNSUPPORTED;
-    return PN_OK;
-}
-
-bool aligned4(const void *p) { return ((uintptr_t)p & 3) == 0; }
 
 Prob make_prob(int t, const void *W, int64_t N, int64_t K, const void *x, float *y)
 {
@@ -701,32 +582,6 @@ pn_status pn_gemv2(pn_type t, const void *W0, const void *W1, int64_t N, int64_t
     return launch_stream(a, lds, stream_v2(p0), s, kVarStream);
 }
 
-pn_status pn_gemm_smallm(pn_type t, const void *W, int64_t N, int64_t K, const void *X, int64_t ldx, int M,
-                         float *Y, int64_t ldy, void *stream)
-{
-    pn_status st = check_matrix(t, W, N, K);
-    if (st) return st;
-    if (!X || !Y) return PN_EINVAL;
-    if (M < 1 || M > 8 || ldx < K || ldy < N || (ldx & 1)) return PN_ESHAPE;
-    if (!aligned4(X) || !aligned4(Y)) return PN_EALIGN;
-    hipStream_t s = (hipStream_t)stream;
-    const int nw = (int)(K / wpb(t) * 8);
-    const DeviceInfo &d = device_info();
-    constexpr int R = 2;
-    const int tiles = (int)((N + kWaves * R - 1) / (kWaves * R));
-    int grid = d.cus * 2;
-    if (grid > tiles) grid = tiles;
-    if (t == PN_PN3T)
-        hipLaunchKernelGGL((gemm_smallm<0, 8, R>), dim3(grid), dim3(kThreads), 0, s, (const uint8_t *)W, (int)N,
-                           nw, (const uint8_t *)X, ldx * 2, M, Y, ldy);
-    else
-        hipLaunchKernelGGL((gemm_smallm<1, 8, R>), dim3(grid), dim3(kThreads), 0, s, (const uint8_t *)W, (int)N,
-                           nw, (const uint8_t *)X, ldx * 2, M, Y, ldy);
-    if (hipGetLastError() != hipSuccess) return PN_ELAUNCH;
-    g_last_variant = kVarSmallM;
-    return PN_OK;
-}
-
 pn_status pn_dequantize(pn_type t, const void *W, int64_t N, int64_t K, float *out, void *stream)
 {
     pn_status st = check_matrix(t, W, N, K);
@@ -745,14 +600,6 @@ pn_status pn_dequantize(pn_type t, const void *W, int64_t N, int64_t K, float *o
     g_last_variant = kVarDequant;
     return PN_OK;
 }
-
-struct pn_group {
-    Prob *table;      // device
-    int count;
-    int total_tiles;
-    int lds;
-    bool v2;
-};
 
 pn_status pn_group_create(const pn_gemv_desc *descs, int count, pn_group **out)
 {
@@ -788,7 +635,7 @@ pn_status pn_group_create(const pn_gemv_desc *descs, int count, pn_group **out)
         free(host);
         return PN_ENOMEM;
     }
-    if (hipMalloc((void **)&g->table, sizeof(Prob) * (size_t)count) != hipSuccess) {
+    if (hipMalloc(&g->table, sizeof(Prob) * (size_t)count) != hipSuccess) {
         free(host);
         free(g);
         return PN_ENOMEM;
@@ -800,10 +647,11 @@ pn_status pn_group_create(const pn_gemv_desc *descs, int count, pn_group **out)
         return PN_ELAUNCH;
     }
     free(host);
+    g->kind = kGroupGemv;
     g->count = count;
     g->total_tiles = (int)tiles;
     g->lds = lds;
-    g->v2 = v2;
+    g->flags = v2 ? 1 : 0;
     *out = g;
     return PN_OK;
 }
@@ -811,12 +659,13 @@ pn_status pn_group_create(const pn_gemv_desc *descs, int count, pn_group **out)
 pn_status pn_group_run(const pn_group *g, void *stream)
 {
     if (!g) return PN_EINVAL;
+    if (g->kind == kGroupSmallM) return smallm_group_run(g, (hipStream_t)stream);
     StreamArgs a;
     memset(&a, 0, sizeof(a));
-    a.table = g->table;
+    a.table = (const Prob *)g->table;
     a.count = g->count;
     a.total_tiles = g->total_tiles;
-    return launch_stream(a, g->lds, g->v2, (hipStream_t)stream, kVarGroupStream);
+    return launch_stream(a, g->lds, g->flags != 0, (hipStream_t)stream, kVarGroupStream);
 }
 
 void pn_group_destroy(pn_group *g)
@@ -849,7 +698,10 @@ const char *pn_variant_name(int v)
     case kVarNone: return "none";
     case kVarStream: return "gemv_stream";
     case kVarGeneric: return "gemv_generic";
-    case kVarSmallM: return "gemm_smallm_valu";
+    case kVarSmallMValu: return "gemm_stream_valu";
+    case kVarSmallMMfma: return "gemm_stream_mfma";
+    case kVarGroupSmallMValu: return "gemm_stream_valu_group";
+    case kVarGroupSmallMMfma: return "gemm_stream_mfma_group";
     case kVarDequant: return "dequant";
     case kVarGroupStream: return "gemv_stream_group";
     }

@@ -1,0 +1,580 @@
+// pn_smallm.hip - small-batch PN GEMM (M <= 8 activation rows) for AMD
+// Instinct MI355X (gfx950), and its C ABI: pn_gemm_smallm,
+// pn_group_create_smallm, pn_set_smallm_math.
+//
+// Y[m, r] = sum_k w[r, k] X[m, k] for m < M <= 8, the verification width of
+// speculative decoding (v100-skinny README, "How QPN works": an 8-row tile
+// costs the same whether or not every row carries work).  Each weight is
+// decoded once and used for all M rows.
+//
+// Work layout.  A wave owns 32 consecutive rows (two groups of 16) and walks
+// their blocks in order, with a pipeline of U blocks of loads in flight.
+// Lane l = 16 g + j loads words 2g and 2g+1 (one dwordx2) of row j of each
+// group, plus that block's scale.  The workgroup's activations sit in LDS,
+// a chunk of whole blocks at a time.
+//
+// Two maths over the same loads (pn_set_smallm_math):
+//   MFMA  the decoded weights of 16 rows x one block form the B operand of
+//         v_mfma_f32_16x16x16_f16 (pn3t: 5 steps per block) or
+//         v_mfma_f32_16x16x32_f16 (pn4t: 2 steps); X is the A operand, its
+//         rows 8..15 repeating rows 0..7 (their results are discarded).  Each
+//         block starts a fresh accumulator, which is scaled by that block's d
+//         in fp32 and added to the running sum: folding d into fp16 operands
+//         would round.  Lane (j, g) receives D[m = 4g + i][row j], i < 4, so
+//         one scale per lane serves all four.
+//   VALU  each lane dots its 20 (pn3t) or 16 (pn4t) decoded weights with each
+//         of the M activation rows (v_dot2_f32_f16), scales by d and keeps M
+//         sums per row; the four lanes of a row are added at the end.
+// Within a block, lane g's weights are the block's 20g..20g+19 (pn3t: words
+// 2g and 2g+1 hold ten consecutive weights each) or 16g..16g+15 (pn4t), and
+// the X operand is read at the same positions, so both maths pair every code
+// with its own activation.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "pn_device.h"
+#include "pn_host.h"
+
+using namespace pn;
+using namespace pn::host;
+
+namespace {
+
+#ifndef PN_SM_WAVES
+#define PN_SM_WAVES 8
+#endif
+#ifndef PN_SM_ITEMS
+#define PN_SM_ITEMS 4
+#endif
+// LDS budget of one workgroup's activation chunk, in KiB.
+#ifndef PN_SM_LDS_KB
+#define PN_SM_LDS_KB 64
+#endif
+
+constexpr int kSmWaves = PN_SM_WAVES;
+constexpr int kSmThreads = 64 * kSmWaves;
+constexpr int kSmU = PN_SM_ITEMS;
+constexpr int kWaveRows = 32;
+constexpr int kTileRows = kSmWaves * kWaveRows;
+constexpr int kSmLdsMax = PN_SM_LDS_KB * 1024;
+constexpr int kMaxM = 8;
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// One small-M problem as the device sees it.
+struct SmProb {
+    const uint8_t *W;  // packed rows
+    const uint8_t *X;  // fp16; row m at X + 2 * ldx * m
+    float *Y;          // fp32; row m at Y + ldy * m
+    int64_t ldx, ldy;  // leading dimensions, elements
+    int32_t N, nb;     // rows, blocks per row
+    int32_t M, type;
+    int32_t tile0;     // first tile of this problem in the launch
+    int32_t cb;        // blocks per activation chunk
+    int32_t nchunks;
+    int32_t stride;    // LDS bytes per staged activation row (multiple of 256)
+};
+
+struct SmArgs {
+    const SmProb *table;  // device table, or null for the single problem p0
+    SmProb p0;
+    int32_t count;
+    int32_t total_tiles;
+};
+
+// LDS address of byte o of staged activation row m.  Rows are `stride` bytes
+// apart (a multiple of 256).  The XOR moves 32-byte (pn3t) or 16-byte (pn4t)
+// pieces inside a 256-byte window so that the 32 distinct reads of one
+// operand load (8 rows x 4 lane groups) spread over the banks: pn3t reads 8
+// bytes at 40g + 8s, pn4t 16 bytes at 32g + 16s.
+template <int TYPE>
+__device__ __forceinline__ uint32_t xoff(uint32_t m, uint32_t stride, uint32_t o)
+{
+    const uint32_t sw = TYPE == 0 ? (m << 5) : (((m & 1u) << 7) | ((m & 2u) << 3));
+    return m * stride + (o ^ sw);
+}
+
+// Stage activation blocks [b0, b0 + nbc) of all M rows into LDS.  The loads
+// are buffer loads like the weight loads: mixing in global (FLAT-family)
+// loads makes the compiler's wait analysis drain every load in flight at the
+// pipeline's loop head.
+template <int TYPE>
+__device__ __forceinline__ void stage_chunk(const SmProb &p, int b0, int nbc, uint8_t *lds)
+{
+    constexpr int W = Fmt<TYPE>::W;
+    const int per_row = nbc * (W / 8);  // 16-byte pieces per row
+    const int total = p.M * per_row;
+    const int row_stride = (int)(2 * p.ldx);
+    const __amdgpu_buffer_rsrc_t xr =
+        make_rsrc(uniform_ptr(p.X + (size_t)2 * b0 * W), (uint32_t)(row_stride * (p.M - 1) + 16 * per_row));
+    for (int i = threadIdx.x; i < total; i += kSmThreads) {
+        const int m = i / per_row, q = i - m * per_row;
+        const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, row_stride * m + 16 * q, 0, 0));
+        *(u32x4 *)(lds + xoff<TYPE>((uint32_t)m, (uint32_t)p.stride, 16u * q)) = v;
+    }
+}
+
+// One wave's 32 rows of problem p, all blocks.  Every wave of the workgroup
+// calls this with the same problem (chunk restaging uses workgroup barriers).
+template <int TYPE, bool MFMA>
+__device__ __forceinline__ void sm_tile(const SmProb &p, int row0, uint8_t *lds)
+{
+    constexpr int P = Unpack<TYPE>::kPairs;
+    constexpr int U = kSmU;
+    const int lane = threadIdx.x & 63;
+    const int j = lane & 15, g = lane >> 4;
+    const int nb = uniform(p.nb), cb = uniform(p.cb), M = uniform(p.M);
+    const uint32_t stride = (uint32_t)uniform(p.stride);
+    const int row_bytes = 34 * nb;
+    const int valid = uniform(p.N - row0 < kWaveRows ? p.N - row0 : kWaveRows);  // <= 0: no rows
+    // Loads go through a buffer resource over the wave's valid rows: rows past
+    // N read zeros.
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(uniform_ptr(p.W + (size_t)(valid > 0 ? row0 : 0) * row_bytes),
+                  valid > 0 ? (uint32_t)valid * (uint32_t)row_bytes : 0u);
+    const int vs0 = j * row_bytes, vs1 = vs0 + 16 * row_bytes;  // block scale, rows j and 16 + j
+    const int vw0 = vs0 + 2 + 8 * g, vw1 = vw0 + 16 * row_bytes;  // words 2g, 2g + 1
+    const uint32_t ma = (uint32_t)(j & 7) < (uint32_t)M ? (uint32_t)(j & 7) : 0u;  // A row (MFMA)
+
+    uint32_t qw[U][2][2], qs[U][2];
+    float4_t accm[2];
+    float accv[2][kMaxM];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        accm[r] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int m = 0; m < kMaxM; ++m) accv[r][m] = 0.0f;
+    }
+    int ib = 0;                         // next block to load
+    int ic = 0;                         // next block to use
+    int cbase = 0;                      // first block of the staged chunk
+    int cnext = cb < nb ? cb : nb + 1;  // block at which the next chunk is staged
+
+    auto issue = [&](int slot) {
+        const int soff = 34 * ib;
+        const auto a = __builtin_amdgcn_raw_buffer_load_b64(rs, vw0, soff, 0);
+        const auto b = __builtin_amdgcn_raw_buffer_load_b64(rs, vw1, soff, 0);
+        qw[slot][0][0] = a[0];
+        qw[slot][0][1] = a[1];
+        qw[slot][1][0] = b[0];
+        qw[slot][1][1] = b[1];
+        qs[slot][0] = __builtin_amdgcn_raw_buffer_load_b16(rs, vs0, soff, 0);
+        qs[slot][1] = __builtin_amdgcn_raw_buffer_load_b16(rs, vs1, soff, 0);
+        ++ib;
+    };
+    // Chunk boundaries are multiples of U blocks: the restage is checked once
+    // per group of U blocks, outside the per-block code, so that the loads in
+    // flight stay in their registers across it.
+    auto restage = [&]() {
+        if (ic == cnext) {
+            __syncthreads();
+            stage_chunk<TYPE>(p, ic, nb - ic < cb ? nb - ic : cb, lds);
+            __syncthreads();
+            cbase = ic;
+            cnext = ic + cb;
+        }
+    };
+    auto consume = [&](int slot) {
+        const uint32_t bl = (uint32_t)(ic - cbase);
+        half2_t t[2][2][P];
+        float d[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            Unpack<TYPE>::run(qw[slot][r][0], t[r][0]);
+            Unpack<TYPE>::run(qw[slot][r][1], t[r][1]);
+            d[r] = half_bits_to_float(qs[slot][r]);
+        }
+        if constexpr (MFMA) {
+            if constexpr (TYPE == 0) {
+                half4_t a[5];
+#pragma unroll
+                for (int s = 0; s < 5; ++s)
+                    a[s] = __builtin_bit_cast(
+                        half4_t, *(const u32x2 *)(lds + xoff<0>(ma, stride, 160u * bl + 40u * g + 8u * s)));
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    // pairs 0..4 from word 2g, 5..9 from word 2g + 1; step s takes pairs 2s, 2s + 1
+                    const half2_t *u = t[r][0];
+                    const half2_t *v = t[r][1];
+                    float4_t D = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                        a[0], __builtin_shufflevector(u[0], u[1], 0, 1, 2, 3), (float4_t){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                    D = __builtin_amdgcn_mfma_f32_16x16x16f16(a[1], __builtin_shufflevector(u[2], u[3], 0, 1, 2, 3), D, 0, 0, 0);
+                    D = __builtin_amdgcn_mfma_f32_16x16x16f16(a[2], __builtin_shufflevector(u[4], v[0], 0, 1, 2, 3), D, 0, 0, 0);
+                    D = __builtin_amdgcn_mfma_f32_16x16x16f16(a[3], __builtin_shufflevector(v[1], v[2], 0, 1, 2, 3), D, 0, 0, 0);
+                    D = __builtin_amdgcn_mfma_f32_16x16x16f16(a[4], __builtin_shufflevector(v[3], v[4], 0, 1, 2, 3), D, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) accm[r][i] = __builtin_fmaf(D[i], d[r], accm[r][i]);
+                }
+            } else {
+                half8_t a[2];
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    a[s] = __builtin_bit_cast(
+                        half8_t, *(const u32x4 *)(lds + xoff<1>(ma, stride, 128u * bl + 32u * g + 16u * s)));
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    const half2_t *u = t[r][0];
+                    const half2_t *v = t[r][1];
+                    const half8_t b0 = __builtin_shufflevector(__builtin_shufflevector(u[0], u[1], 0, 1, 2, 3),
+                                                               __builtin_shufflevector(u[2], u[3], 0, 1, 2, 3), 0, 1,
+                                                               2, 3, 4, 5, 6, 7);
+                    const half8_t b1 = __builtin_shufflevector(__builtin_shufflevector(v[0], v[1], 0, 1, 2, 3),
+                                                               __builtin_shufflevector(v[2], v[3], 0, 1, 2, 3), 0, 1,
+                                                               2, 3, 4, 5, 6, 7);
+                    float4_t D = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], b0, (float4_t){0.0f, 0.0f, 0.0f, 0.0f},
+                                                                        0, 0, 0);
+                    D = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[1], b1, D, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) accm[r][i] = __builtin_fmaf(D[i], d[r], accm[r][i]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < kMaxM; ++m) {
+                if (m < M) {
+                    uint32_t xp[2 * P];
+                    if constexpr (TYPE == 0) {
+#pragma unroll
+                        for (int s = 0; s < 5; ++s) {
+                            const u32x2 v = *(const u32x2 *)(lds + xoff<0>((uint32_t)m, stride, 160u * bl + 40u * g + 8u * s));
+                            xp[2 * s] = v[0];
+                            xp[2 * s + 1] = v[1];
+                        }
+                    } else {
+#pragma unroll
+                        for (int s = 0; s < 2; ++s) {
+                            const u32x4 v = *(const u32x4 *)(lds + xoff<1>((uint32_t)m, stride, 128u * bl + 32u * g + 16u * s));
+                            xp[4 * s] = v[0];
+                            xp[4 * s + 1] = v[1];
+                            xp[4 * s + 2] = v[2];
+                            xp[4 * s + 3] = v[3];
+                        }
+                    }
+#pragma unroll
+                    for (int r = 0; r < 2; ++r) {
+                        const float part = dot_pairs(t[r][1], xp + P, dot_pairs0(t[r][0], xp));
+                        accv[r][m] = __builtin_fmaf(d[r], part, accv[r][m]);
+                    }
+                }
+            }
+        }
+        ++ic;
+    };
+
+    if (nb >= 2 * U) {
+        // Slots are issued in order, so that each slot's wait covers its own
+        // loads only.
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            issue(u);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        int done = 0;
+        do {
+            restage();
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                consume(u);
+                __builtin_amdgcn_sched_barrier(0);
+                issue(u);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            done += U;
+        } while (done + 2 * U <= nb);
+        restage();
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            consume(u);
+            if (done + u + U < nb) issue(u);
+        }
+        restage();
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (done + U + u < nb) consume(u);
+    } else {
+        for (int i = 0; i < nb; ++i) {
+            if (i % U == 0) restage();
+            issue(0);
+            consume(0);
+        }
+    }
+
+    if constexpr (MFMA) {
+        // lane (j, g) holds D[m = 4g + i][row j]; lanes g = 2, 3 hold the repeated rows
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 4 * g + i, row = 16 * r + j;
+                if (g < 2 && m < M && row < valid) p.Y[p.ldy * m + row0 + row] = accm[r][i];
+            }
+    } else {
+        // add the four lanes of each row; lane (j, g) stores m = g and g + 4
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int m = 0; m < kMaxM; ++m) {
+                if (m < M) {
+                    float v = accv[r][m];
+                    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+                    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+                    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+                    v = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+                    const int row = 16 * r + j;
+                    if ((m & 3) == g && row < valid) p.Y[p.ldy * m + row0 + row] = v;
+                }
+            }
+    }
+    // Drain the stores before the next tile's loads (one counter covers both
+    // on gfx9; a pending store would turn every wait of the next pipeline into
+    // a full drain).
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+}
+
+__device__ __forceinline__ const SmProb *sm_problem(const SmArgs &a, int i)
+{
+    return a.table ? a.table + i : &a.p0;
+}
+
+__device__ __forceinline__ int sm_tile0(const SmArgs &a, int i)
+{
+    if (i >= a.count) return a.total_tiles;
+    return a.table ? a.table[i].tile0 : a.p0.tile0;
+}
+
+// Workgroups take tiles (kSmWaves x 32 rows of one problem) in a grid
+// stride.  The activation chunk is restaged when the problem changes, and at
+// every chunk boundary of problems whose activations do not fit at once.
+template <bool MFMA>
+__global__ __launch_bounds__(kSmThreads) void gemm_stream(SmArgs args)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int wave = uniform(threadIdx.x >> 6);
+    int i = 0, next0 = -1, staged = -1;
+    SmProb p;
+    for (int tile = blockIdx.x; tile < args.total_tiles; tile += gridDim.x) {
+        if (tile >= next0) {
+            if (next0 >= 0) ++i;
+            while (sm_tile0(args, i + 1) <= tile) ++i;
+            const SmProb &c = *sm_problem(args, i);
+            p.W = uniform_ptr(c.W);
+            p.X = uniform_ptr(c.X);
+            p.Y = uniform_ptr(c.Y);
+            p.ldx = ((int64_t)uniform((int32_t)(c.ldx >> 32)) << 32) | (uint32_t)uniform((int32_t)c.ldx);
+            p.ldy = ((int64_t)uniform((int32_t)(c.ldy >> 32)) << 32) | (uint32_t)uniform((int32_t)c.ldy);
+            p.N = uniform(c.N);
+            p.nb = uniform(c.nb);
+            p.M = uniform(c.M);
+            p.type = uniform(c.type);
+            p.tile0 = uniform(c.tile0);
+            p.cb = uniform(c.cb);
+            p.nchunks = uniform(c.nchunks);
+            p.stride = uniform(c.stride);
+            next0 = uniform(sm_tile0(args, i + 1));
+        }
+        if (p.nchunks > 1 || staged != i) {
+            const int nbc = p.nb < p.cb ? p.nb : p.cb;
+            __syncthreads();
+            if (p.type == 0)
+                stage_chunk<0>(p, 0, nbc, lds);
+            else
+                stage_chunk<1>(p, 0, nbc, lds);
+            __syncthreads();
+        }
+        staged = p.nchunks > 1 ? -1 : i;
+        const int row0 = ((tile - p.tile0) * kSmWaves + wave) * kWaveRows;
+        if (p.type == 0)
+            sm_tile<0, MFMA>(p, row0, lds);
+        else
+            sm_tile<1, MFMA>(p, row0, lds);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+int g_math = PN_SMALLM_MFMA;  // process-wide choice of pn_set_smallm_math
+
+struct SmDevice {
+    int ready = 0;
+    signed char occ[2][161];  // workgroups per CU by math and LDS KiB (0 = not queried)
+};
+SmDevice g_sm[64];
+
+int sm_wgs_per_cu(bool mfma, int lds)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    SmDevice &d = g_sm[dev];
+    if (!d.ready) {
+        memset(d.occ, 0, sizeof(d.occ));
+        // activation chunks above 64 KiB need the kernels' LDS limit raised
+        (void)hipFuncSetAttribute((const void *)gemm_stream<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  kSmLdsMax);
+        (void)hipFuncSetAttribute((const void *)gemm_stream<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  kSmLdsMax);
+        d.ready = 1;
+    }
+    int q = (lds + 1023) / 1024;
+    q = q < 0 ? 0 : (q > 160 ? 160 : q);
+    signed char &o = d.occ[mfma ? 1 : 0][q];
+    if (o == 0) {
+        int occ = 0;
+        const hipError_t e = mfma ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_stream<true>, kSmThreads,
+                                                                                  (size_t)q * 1024)
+                                  : hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_stream<false>, kSmThreads,
+                                                                                  (size_t)q * 1024);
+        if (e != hipSuccess || occ <= 0) occ = 1;
+        o = (signed char)(occ > 127 ? 127 : occ);
+    }
+    return o;
+}
+
+// Fill an SmProb for one problem (validated) and choose its activation
+// chunking: the fewest chunks of whole blocks whose M staged rows fit the LDS
+// budget, equal in size up to U blocks (every boundary a multiple of U).
+pn_status sm_make(int t, const void *W, int64_t N, int64_t K, const void *X, int64_t ldx, int M, float *Y,
+                  int64_t ldy, SmProb &p)
+{
+    pn_status st = check_matrix(t, W, N, K);
+    if (st) return st;
+    if (!X || !Y) return PN_EINVAL;
+    if (M < 1 || M > kMaxM || ldx < K || ldy < N || (ldx & 1)) return PN_ESHAPE;
+    if (!aligned4(X) || !aligned4(Y)) return PN_EALIGN;
+    if (2 * ldx * M > INT32_MAX) return PN_EUNSUPPORTED;  // activation offsets are 32-bit
+    const int64_t nb = K / wpb(t);
+    if (nb * 34 * kWaveRows > INT32_MAX) return PN_EUNSUPPORTED;  // per-wave offsets are 32-bit
+    const int64_t bytes_per_block = (int64_t)wpb(t) * 2;              // staged bytes per block and row
+    int64_t nchunks = 1, cb = nb, stride = 0;
+    for (;; ++nchunks) {
+        cb = (nb + nchunks - 1) / nchunks;
+        if (cb < nb) cb = (cb + kSmU - 1) / kSmU * kSmU;  // chunk boundaries at multiples of U blocks
+        stride = (cb * bytes_per_block + 255) / 256 * 256;
+        if (stride * M <= kSmLdsMax) break;
+        if (cb <= kSmU) return PN_EUNSUPPORTED;
+    }
+    memset(&p, 0, sizeof(p));
+    p.W = (const uint8_t *)W;
+    p.X = (const uint8_t *)X;
+    p.Y = Y;
+    p.ldx = ldx;
+    p.ldy = ldy;
+    p.N = (int32_t)N;
+    p.nb = (int32_t)nb;
+    p.M = M;
+    p.type = t;
+    p.cb = (int32_t)cb;
+    p.nchunks = (int32_t)((nb + cb - 1) / cb);
+    p.stride = (int32_t)stride;
+    return PN_OK;
+}
+
+int sm_lds(const SmProb &p) { return p.M * p.stride; }
+
+pn_status sm_launch(const SmArgs &a, int lds, bool mfma, hipStream_t s, int variant)
+{
+    int grid = device_cus() * sm_wgs_per_cu(mfma, lds);
+    if (grid > a.total_tiles) grid = a.total_tiles;
+    if (grid < 1) grid = 1;
+    if (mfma)
+        hipLaunchKernelGGL(gemm_stream<true>, dim3(grid), dim3(kSmThreads), lds, s, a);
+    else
+        hipLaunchKernelGGL(gemm_stream<false>, dim3(grid), dim3(kSmThreads), lds, s, a);
+    if (hipGetLastError() != hipSuccess) return PN_ELAUNCH;
+    g_last_variant = variant;
+    return PN_OK;
+}
+
+}  // namespace
+
+pn_status pn::host::smallm_group_run(const pn_group *g, hipStream_t s)
+{
+    SmArgs a;
+    memset(&a, 0, sizeof(a));
+    a.table = (const SmProb *)g->table;
+    a.count = g->count;
+    a.total_tiles = g->total_tiles;
+    const bool mfma = g->flags == PN_SMALLM_MFMA;
+    return sm_launch(a, g->lds, mfma, s, mfma ? kVarGroupSmallMMfma : kVarGroupSmallMValu);
+}
+
+extern "C" {
+
+pn_status pn_set_smallm_math(pn_smallm_math m)
+{
+    if (m != PN_SMALLM_MFMA && m != PN_SMALLM_VALU) return PN_EINVAL;
+    __atomic_store_n(&g_math, (int)m, __ATOMIC_RELAXED);
+    return PN_OK;
+}
+
+pn_smallm_math pn_get_smallm_math(void) { return (pn_smallm_math)__atomic_load_n(&g_math, __ATOMIC_RELAXED); }
+
+pn_status pn_gemm_smallm(pn_type t, const void *W, int64_t N, int64_t K, const void *X, int64_t ldx, int M,
+                         float *Y, int64_t ldy, void *stream)
+{
+    SmArgs a;
+    memset(&a, 0, sizeof(a));
+    pn_status st = sm_make(t, W, N, K, X, ldx, M, Y, ldy, a.p0);
+    if (st) return st;
+    const int64_t tiles = (N + kTileRows - 1) / kTileRows;
+    a.count = 1;
+    a.total_tiles = (int32_t)tiles;
+    const bool mfma = pn_get_smallm_math() == PN_SMALLM_MFMA;
+    return sm_launch(a, sm_lds(a.p0), mfma, (hipStream_t)stream, mfma ? kVarSmallMMfma : kVarSmallMValu);
+}
+
+pn_status pn_group_create_smallm(const pn_gemm_desc *descs, int count, pn_group **out)
+{
+    if (!descs || !out || count < 1) return PN_EINVAL;
+    *out = nullptr;
+    SmProb *host = (SmProb *)calloc((size_t)count, sizeof(SmProb));
+    if (!host) return PN_ENOMEM;
+    int lds = 0;
+    int64_t tiles = 0;
+    pn_status st = PN_OK;
+    for (int i = 0; i < count && st == PN_OK; ++i) {
+        const pn_gemm_desc &e = descs[i];
+        st = sm_make(e.type, e.W, e.N, e.K, e.X, e.ldx, e.M, e.Y, e.ldy, host[i]);
+        if (st != PN_OK) break;
+        host[i].tile0 = (int32_t)tiles;
+        tiles += (e.N + kTileRows - 1) / kTileRows;
+        if (tiles > INT32_MAX) st = PN_EUNSUPPORTED;
+        if (sm_lds(host[i]) > lds) lds = sm_lds(host[i]);
+    }
+    if (st != PN_OK) {
+        free(host);
+        return st;
+    }
+    pn_group *g = (pn_group *)calloc(1, sizeof(pn_group));
+    if (!g) {
+        free(host);
+        return PN_ENOMEM;
+    }
+    if (hipMalloc(&g->table, sizeof(SmProb) * (size_t)count) != hipSuccess) {
+        free(host);
+        free(g);
+        return PN_ENOMEM;
+    }
+    if (hipMemcpy(g->table, host, sizeof(SmProb) * (size_t)count, hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipFree(g->table);
+        free(host);
+        free(g);
+        return PN_ELAUNCH;
+    }
+    free(host);
+    g->kind = kGroupSmallM;
+    g->count = count;
+    g->total_tiles = (int)tiles;
+    g->lds = lds;
+    g->flags = pn_get_smallm_math();
+    *out = g;
+    return PN_OK;
+}
+
+}  // extern "C"

@@ -9,8 +9,9 @@ GEMVs on the current stream in one of these launch schedules:
   layer  four launches per layer, the groups a real decoder can form because
          their inputs are ready together: {q, k, v}, {o}, {gate, up}, {down};
   gemv   one pn_gemv launch per matrix.
-With M > 1 every matrix is one pn_gemm_smallm launch.  A schedule can be
-captured once into a HIP graph (torch.cuda.CUDAGraph) and replayed.
+With M > 1 the token schedule is one pn_group_create_smallm plan and the gemv
+schedule one pn_gemm_smallm launch per matrix.  A schedule can be captured
+once into a HIP graph (torch.cuda.CUDAGraph) and replayed.
 """
 import numpy as np
 import torch
@@ -52,13 +53,16 @@ class Sweep:
 
     # -- schedules --------------------------------------------------------
     def _problem(self, e):
+        if self.m is not None:
+            return (e["type"], e["W"], e["N"], e["K"], e["x"], e["K"], self.m, e["y"], e["N"])
         return (e["type"], e["W"], e["N"], e["K"], e["x"], e["y"])
 
     def prepare(self, schedule):
-        if self.m is not None and schedule != "gemv":
-            raise ValueError("M > 1 runs the gemv schedule only")
+        if self.m is not None and schedule == "layer":
+            raise ValueError("M > 1 runs the token and gemv schedules")
         if schedule == "token" and "token" not in self.groups:
-            self.groups["token"] = [B.Group([self._problem(e) for e in self.mats])]
+            self.groups["token"] = [B.Group([self._problem(e) for e in self.mats],
+                                            smallm=self.m is not None)]
         if schedule == "layer" and "layer" not in self.groups:
             gl = []
             per = len(synth.SWEEP_LAYER)

@@ -81,14 +81,31 @@ pn_status pn_gemv2(pn_type t, const void *W0, const void *W1, int64_t N,
 /* Small-batch product for M <= 8 activation rows (speculative-decoding
  * verification width; v100-skinny README, "How QPN works"):
  * Y[m*ldy + r] = sum_k w[r,k] * X[m*ldx + k] for m < M, r < N.
- * Each weight is decoded once and used M times.
+ * Each weight is decoded exactly once and used M times; products accumulate
+ * in fp32, within 1e-5 * sum_k |w[r,k] X[m,k]| of the exact value.
  *   X : M rows of fp16, leading dimension ldx >= K (elements), 4-byte aligned,
  *       ldx even
  *   Y : M rows of fp32, leading dimension ldy >= N (elements), overwritten
- *   M : 1..8 */
+ *   M : 1..8
+ * The arithmetic unit is the one pn_set_smallm_math selected. */
 pn_status pn_gemm_smallm(pn_type t, const void *W, int64_t N, int64_t K,
                          const void *X, int64_t ldx, int M,
                          float *Y, int64_t ldy, void *stream);
+
+/* Arithmetic of the small-batch kernels.  Both read the weights the same way
+ * and agree within the tolerance above:
+ *   PN_SMALLM_MFMA  decoded weights feed matrix-core products
+ *                   (v_mfma_f32_16x16x16_f16 / 16x16x32_f16), one per block
+ *                   and 16 rows, each scaled by its block's d in fp32; the
+ *                   default (faster on MI355X at M = 8);
+ *   PN_SMALLM_VALU  per-lane fp16 dot products (v_dot2_f32_f16) reduced
+ *                   across the lanes of a row.
+ * The setting is process-wide and read when a call is made or a group is
+ * created (a group keeps the choice it was created with).  Returns PN_EINVAL
+ * for an unknown value. */
+typedef enum { PN_SMALLM_MFMA = 0, PN_SMALLM_VALU = 1 } pn_smallm_math;
+pn_status pn_set_smallm_math(pn_smallm_math m);
+pn_smallm_math pn_get_smallm_math(void);
 
 /* Dense fp32 copy of the decoded weights, out[r*K + k] = d * (n - z),
  * bit-exact with the format's definition ("Exact decode in fp32": no
@@ -121,7 +138,24 @@ typedef struct pn_group pn_group;
  * return PN_EUNSUPPORTED (pn_gemv takes them one at a time). */
 pn_status pn_group_create(const pn_gemv_desc *descs, int count, pn_group **out);
 
-/* Enqueue all GEMVs of the plan as one launch on `stream`. */
+/* The small-batch counterpart: each entry is one pn_gemm_smallm problem
+ * (arguments and checks as there), all run by one launch.  Any K is taken.
+ * Allocation and lifetime as for pn_group_create. */
+typedef struct pn_gemm_desc {
+    const void *W;   /* packed rows, device                     */
+    const void *X;   /* fp16 [M][ldx], device                   */
+    float *Y;        /* fp32 [M][ldy], device, overwritten      */
+    int64_t N;
+    int64_t K;
+    int64_t ldx;     /* elements, >= K, even                    */
+    int64_t ldy;     /* elements, >= N                          */
+    int32_t type;    /* pn_type                                 */
+    int32_t M;       /* 1..8                                    */
+} pn_gemm_desc;
+
+pn_status pn_group_create_smallm(const pn_gemm_desc *descs, int count, pn_group **out);
+
+/* Enqueue all problems of a plan (either kind) as one launch on `stream`. */
 pn_status pn_group_run(const pn_group *g, void *stream);
 
 /* Free a plan (NULL is allowed).  Synchronises the device first. */

@@ -93,3 +93,31 @@ def test_group_host_checks():
     assert lib.pn_group_create(None, 1, ctypes.byref(h)) == PN_EINVAL
     assert lib.pn_group_run(None, None) == PN_EINVAL
     lib.pn_group_destroy(None)
+
+
+def test_smallm_group_host_checks():
+    ok = ("pn3t", FAKE, 4, 80, FAKE, 80, 2, FAKE, 4)
+    bad = [
+        (("pn3t", FAKE, 4, 80, FAKE, 80, 9, FAKE, 4), PN_ESHAPE),      # M > 8
+        (("pn3t", FAKE, 4, 80, FAKE, 81, 2, FAKE, 4), PN_ESHAPE),      # odd ldx
+        (("pn4t", FAKE, 4, 80, FAKE, 80, 2, FAKE, 4), PN_ESHAPE),      # K not whole pn4t blocks
+        (("pn3t", FAKE, 4, 80, FAKE + 2, 80, 2, FAKE, 4), PN_EALIGN),  # X
+        (("pn3t", FAKE, 4, 80, FAKE, 80, 2, None, 4), PN_EINVAL),
+    ]
+    for args, status in bad:
+        with pytest.raises(B.PNError) as e:
+            B.Group([ok, args], smallm=True)
+        assert e.value.status == status, args
+    lib = B.lib()
+    h = ctypes.c_void_p()
+    assert lib.pn_group_create_smallm(None, 1, ctypes.byref(h)) == PN_EINVAL
+
+
+def test_smallm_math_setting():
+    assert B.pn_get_smallm_math() == "mfma"
+    assert B.pn_set_smallm_math(7, check=False) == PN_EINVAL
+    assert B.pn_get_smallm_math() == "mfma"
+    B.pn_set_smallm_math("valu")
+    assert B.pn_get_smallm_math() == "valu"
+    B.pn_set_smallm_math("mfma")
+    assert B.pn_get_smallm_math() == "mfma"

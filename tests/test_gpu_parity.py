@@ -232,28 +232,109 @@ def test_group_mixed():
 
 
 # ---------------------------------------------------------------------------
-# small M
+# small M (both arithmetic units over the same loads)
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("t,n,k", [("pn3t", 256, 5120), ("pn4t", 300, 17408), ("pn4t", 33, 6144),
-                                   ("pn3t", 7, 80), ("pn4t", 19, 64 * 9)])
+MATHS = ["mfma", "valu"]
+# (type, N, K): several 32-row wave tiles with ragged tails, rows shorter than
+# the 2U-block pipeline (1 and 7 blocks), and activations that take several
+# LDS chunks at M = 8 (pn3t K = 5120: 2 chunks; pn4t K = 17408: 5 chunks).
+SMALLM_SHAPES = [("pn3t", 256, 5120), ("pn4t", 300, 17408), ("pn4t", 33, 6144), ("pn3t", 7, 80),
+                 ("pn4t", 19, 64 * 9), ("pn3t", 45, 80 * 7), ("pn4t", 1000, 5120)]
+
+
+@pytest.fixture
+def smallm_math(request):
+    B.pn_set_smallm_math(request.param)
+    yield request.param
+    B.pn_set_smallm_math("mfma")
+
+
+def gpu_smallm(t, w, n, k, X, m, ldx, ldy):
+    Y = torch.full((m, ldy), 7.0, dtype=torch.float32, device="cuda")
+    B.pn_gemm_smallm(t, dev(w), n, k, dev(X), ldx, m, Y, ldy)
+    sync()
+    return Y.cpu().numpy()
+
+
+@pytest.mark.parametrize("smallm_math", MATHS, indirect=True)
+@pytest.mark.parametrize("t,n,k", SMALLM_SHAPES)
 @pytest.mark.parametrize("m", [1, 2, 5, 8])
-def test_gemm_smallm(t, n, k, m):
+def test_gemm_smallm(smallm_math, t, n, k, m):
     w, g = random_matrix(n + k + m, t, n, k)
     ldx, ldy = k + 2 * (m % 2), n + 3
     X = np.zeros((m, ldx), np.float16)
     X[:, :k] = synth.activation(g, k, m)
-    say("gemm_smallm %s %dx%d M=%d" % (t, n, k, m))
-    Y = torch.full((m, ldy), 7.0, dtype=torch.float32, device="cuda")
-    B.pn_gemm_smallm(t, dev(w), n, k, dev(X), ldx, m, Y, ldy)
-    sync()
-    Y = Y.cpu().numpy()
+    say("gemm_smallm %s %s %dx%d M=%d" % (smallm_math, t, n, k, m))
+    Y = gpu_smallm(t, w, n, k, X, m, ldx, ldy)
+    assert B.pn_variant_name(B.pn_last_variant()) == "gemm_stream_" + smallm_math
     assert np.all(Y[:, n:] == 7.0), "wrote past N in a row of Y"
     y64, a = pnref.gemm_f64(t, w, n, k, X[:, :k])
-    assert_gemv_close(Y[:, :n], y64, a, "smallm %s M=%d" % (t, m))
+    assert_gemv_close(Y[:, :n], y64, a, "smallm %s %s M=%d" % (smallm_math, t, m))
     if m == 1:
         y1 = gpu_gemv(t, w, n, k, X[0, :k])
         # both within TOL of the fp64 sum, so within 2 * TOL of each other
         assert_gemv_close(Y[0, :n], y1.astype(np.float64), a[0], "smallm vs gemv", tol=2 * TOL)
+
+
+@pytest.mark.parametrize("smallm_math", MATHS, indirect=True)
+@pytest.mark.parametrize("t", ["pn3t", "pn4t"])
+def test_smallm_one_hot_exact(smallm_math, t):
+    """Row m of X is one-hot at k_m: Y[m, r] = w[r, k_m] exactly (one exact
+    product, the rest zeros).  Pins the k <-> (block, word, slot) map of the
+    operand layouts, including both words of a lane and the block edges."""
+    wpb = WPB[t]
+    n, k = 70, wpb * 6
+    w, _ = random_matrix(17, t, n, k)
+    ks = [0, 1, wpb // 4 - 1, wpb // 4, wpb // 2 + 3, wpb - 1, wpb, 5 * wpb + wpb - 2]
+    X = np.zeros((8, k), np.float16)
+    for m, km in enumerate(ks):
+        X[m, km] = 1.0
+    say("smallm one-hot %s %s" % (smallm_math, t))
+    Y = gpu_smallm(t, w, n, k, X, 8, k, n)
+    dense = pnref.dequantize(t, w, n, k)
+    for m, km in enumerate(ks):
+        assert_bits_equal(Y[m] + 0.0, dense[:, km] + 0.0, "one-hot m=%d k=%d" % (m, km))
+
+
+@pytest.mark.parametrize("smallm_math", MATHS, indirect=True)
+def test_smallm_deterministic(smallm_math):
+    t, n, k, m = "pn4t", 300, 17408, 8
+    w, g = random_matrix(3, t, n, k)
+    X = synth.activation(g, k, m)
+    say("smallm determinism %s" % smallm_math)
+    y1 = gpu_smallm(t, w, n, k, X, m, k, n)
+    y2 = gpu_smallm(t, w, n, k, X, m, k, n)
+    assert_bits_equal(y1, y2, "two runs")
+
+
+@pytest.mark.parametrize("smallm_math", MATHS, indirect=True)
+def test_smallm_group(smallm_math):
+    """One launch over problems of mixed type, shape, M and leading
+    dimensions; each against the oracle."""
+    specs = [("pn3t", 100, 5120, 8), ("pn4t", 70, 17408, 3), ("pn4t", 300, 6144, 8),
+             ("pn3t", 5, 80, 1), ("pn4t", 260, 5120, 8), ("pn3t", 33, 80 * 9, 6)]
+    host, probs, keep = [], [], []
+    for i, (t, n, k, m) in enumerate(specs):
+        w, g = random_matrix(1000 + i, t, n, k)
+        ldx, ldy = k + 2 * (i % 2), n + 1
+        X = np.zeros((m, ldx), np.float16)
+        X[:, :k] = synth.activation(g, k, m)
+        Y = torch.full((m, ldy), 7.0, dtype=torch.float32, device="cuda")
+        wd, xd = dev(w), dev(X)
+        keep += [wd, xd]
+        probs.append((t, wd, n, k, xd, ldx, m, Y, ldy))
+        host.append((t, w, n, k, X[:, :k], Y))
+    say("smallm group %s: %d problems" % (smallm_math, len(specs)))
+    grp = B.Group(probs, smallm=True)
+    grp.run()
+    sync()
+    assert B.pn_variant_name(B.pn_last_variant()) == "gemm_stream_%s_group" % smallm_math
+    for t, w, n, k, X, Y in host:
+        Yh = Y.cpu().numpy()
+        assert np.all(Yh[:, n:] == 7.0)
+        y64, a = pnref.gemm_f64(t, w, n, k, X)
+        assert_gemv_close(Yh[:, :n], y64, a, "smallm group %s %dx%d M=%d" % (t, n, k, X.shape[0]))
+    grp.close()
 
 
 def test_read_probe():

@@ -72,15 +72,35 @@ def test_sweep_m1_graph(sweep_m1):
         _check_samples(sw, store)
 
 
-def test_sweep_m8():
+@pytest.fixture(scope="module")
+def sweep_m8():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     store = {}
     say("sweep M=8: generating 64 layers")
     sw = S.Sweep(m=8, sample=lambda rec: S.sample_rows(rec, ROWS, store))
-    say("sweep M=8 run")
-    sw.step("gemv")
-    sync()
-    worst = _check_samples(sw, store, m=8)
-    say("sweep M=8: worst %.3g" % worst)
+    yield sw, store
     sw.close()
+    del sw
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("math", ["mfma", "valu"])
+def test_sweep_m8(sweep_m8, math):
+    """M = 8 over the full sweep: one grouped launch per token (the benchmark's
+    configuration) and one launch per matrix, with the given arithmetic."""
+    sw, store = sweep_m8
+    B.pn_set_smallm_math(math)
+    sw.close()  # plans keep the arithmetic they were created with
+    try:
+        for schedule in ("token", "gemv"):
+            for e in sw.mats:
+                e["y"].fill_(float("nan"))
+            say("sweep M=8 %s schedule %s" % (math, schedule))
+            sw.step(schedule)
+            sync()
+            worst = _check_samples(sw, store, m=8)
+            say("sweep M=8 %s %s: worst %.3g" % (math, schedule, worst))
+    finally:
+        B.pn_set_smallm_math("mfma")
+        sw.close()
