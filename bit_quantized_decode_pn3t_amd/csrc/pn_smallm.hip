@@ -9,7 +9,7 @@
 //
 // Work layout.  A wave owns 32 consecutive rows (two groups of 16) and walks
 // their blocks in order, with a pipeline of U blocks of loads in flight.
-// Lane l = 16 g + j loads words 2g and 2g+1 (one dwordx2) of row j of each
+// Lane l = 4j + g loads words 2g and 2g+1 (one dwordx2) of row j of each
 // group, plus that block's scale.  The workgroup's activations sit in LDS,
 // a chunk of whole blocks at a time.
 //
@@ -20,11 +20,13 @@
 //         rows 8..15 repeating rows 0..7 (their results are discarded).  Each
 //         block starts a fresh accumulator, which is scaled by that block's d
 //         in fp32 and added to the running sum: folding d into fp16 operands
-//         would round.  Lane (j, g) receives D[m = 4g + i][row j], i < 4, so
-//         one scale per lane serves all four.
+//         would round.  The words and scale move to the operand layout (lane
+//         16g + j for row j, k-group g) with ds_bpermute; lane (j, g) then
+//         receives D[m = 4g + i][row j], i < 4, so one scale per lane serves
+//         all four.
 //   VALU  each lane dots its 20 (pn3t) or 16 (pn4t) decoded weights with each
 //         of the M activation rows (v_dot2_f32_f16), scales by d and keeps M
-//         sums per row; the four lanes of a row are added at the end.
+//         sums per row; the four lanes (one quad) of a row are added at the end.
 // Within a block, lane g's weights are the block's 20g..20g+19 (pn3t: words
 // 2g and 2g+1 hold ten consecutive weights each) or 16g..16g+15 (pn4t), and
 // the X operand is read at the same positions, so both maths pair every code
@@ -48,9 +50,22 @@ namespace {
 #ifndef PN_SM_ITEMS
 #define PN_SM_ITEMS 4
 #endif
-// LDS budget of one workgroup's activation chunk, in KiB.
+// MFMA math: loads are issued a group of U blocks at a time into 2U slots, so
+// that each row's next U blocks are requested back to back (measured 3.06 ms
+// vs 3.73 ms per M = 8 token).  The VALU math, bound by its arithmetic, keeps
+// one block at a time in U slots and more waves per CU.
+#ifndef PN_SM_GROUPED
+#define PN_SM_GROUPED 1
+#endif
+// LDS budget of one workgroup's activation chunk, in KiB, per math.  The
+// grouped MFMA pipeline's registers allow one 8-wave workgroup per CU, so it
+// may take the whole LDS (at M = 8 only K > 10240 then needs more than one
+// chunk); the VALU math runs two workgroups per CU.
 #ifndef PN_SM_LDS_KB
-#define PN_SM_LDS_KB 64
+#define PN_SM_LDS_KB 160
+#endif
+#ifndef PN_SM_VALU_LDS_KB
+#define PN_SM_VALU_LDS_KB 80
 #endif
 
 constexpr int kSmWaves = PN_SM_WAVES;
@@ -59,6 +74,7 @@ constexpr int kSmU = PN_SM_ITEMS;
 constexpr int kWaveRows = 32;
 constexpr int kTileRows = kSmWaves * kWaveRows;
 constexpr int kSmLdsMax = PN_SM_LDS_KB * 1024;
+constexpr int kSmLdsValu = PN_SM_VALU_LDS_KB * 1024;
 constexpr int kMaxM = 8;
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
@@ -128,7 +144,16 @@ __device__ __forceinline__ void sm_tile(const SmProb &p, int row0, uint8_t *lds)
     constexpr int P = Unpack<TYPE>::kPairs;
     constexpr int U = kSmU;
     const int lane = threadIdx.x & 63;
-    const int j = lane & 15, g = lane >> 4;
+    // Loads: lane 4j + g reads words 2g, 2g + 1 of row j, so the four lanes of
+    // a quad read 32 contiguous bytes of one row.  (The vector memory pipeline
+    // takes a quad whose lanes fall in different rows one lane at a time; the
+    // MFMA operand layout, where consecutive lanes are consecutive rows, made
+    // every quad of every load touch four rows.)
+    const int j = lane >> 2, g = lane & 3;
+    // MFMA operand layout: lane 16 gm + jm holds row jm, k-group gm; the words
+    // move there with ds_bpermute from lane 4 jm + gm.
+    const int jm = lane & 15, gm = lane >> 4;
+    const int src = 4 * (4 * jm + gm);
     const int nb = uniform(p.nb), cb = uniform(p.cb), M = uniform(p.M);
     const uint32_t stride = (uint32_t)uniform(p.stride);
     const int row_bytes = 34 * nb;
@@ -140,9 +165,11 @@ __device__ __forceinline__ void sm_tile(const SmProb &p, int row0, uint8_t *lds)
                   valid > 0 ? (uint32_t)valid * (uint32_t)row_bytes : 0u);
     const int vs0 = j * row_bytes, vs1 = vs0 + 16 * row_bytes;  // block scale, rows j and 16 + j
     const int vw0 = vs0 + 2 + 8 * g, vw1 = vw0 + 16 * row_bytes;  // words 2g, 2g + 1
-    const uint32_t ma = (uint32_t)(j & 7) < (uint32_t)M ? (uint32_t)(j & 7) : 0u;  // A row (MFMA)
+    const uint32_t ma = (uint32_t)(jm & 7) < (uint32_t)M ? (uint32_t)(jm & 7) : 0u;  // A row (MFMA)
 
-    uint32_t qw[U][2][2], qs[U][2];
+    constexpr bool kGrouped = MFMA && PN_SM_GROUPED;
+    constexpr int S = kGrouped ? 2 * U : U;  // load slots
+    uint32_t qw[S][2][2], qs[S][2];
     float4_t accm[2];
     float accv[2][kMaxM];
 #pragma unroll
@@ -184,11 +211,23 @@ __device__ __forceinline__ void sm_tile(const SmProb &p, int row0, uint8_t *lds)
         const uint32_t bl = (uint32_t)(ic - cbase);
         half2_t t[2][2][P];
         float d[2];
+        if constexpr (MFMA) {
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            Unpack<TYPE>::run(qw[slot][r][0], t[r][0]);
-            Unpack<TYPE>::run(qw[slot][r][1], t[r][1]);
-            d[r] = half_bits_to_float(qs[slot][r]);
+            for (int r = 0; r < 2; ++r) {
+                const uint32_t w0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)qw[slot][r][0]);
+                const uint32_t w1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)qw[slot][r][1]);
+                const uint32_t sc = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)qs[slot][r]);
+                Unpack<TYPE>::run(w0, t[r][0]);
+                Unpack<TYPE>::run(w1, t[r][1]);
+                d[r] = half_bits_to_float(sc);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                Unpack<TYPE>::run(qw[slot][r][0], t[r][0]);
+                Unpack<TYPE>::run(qw[slot][r][1], t[r][1]);
+                d[r] = half_bits_to_float(qs[slot][r]);
+            }
         }
         if constexpr (MFMA) {
             if constexpr (TYPE == 0) {
@@ -196,10 +235,10 @@ __device__ __forceinline__ void sm_tile(const SmProb &p, int row0, uint8_t *lds)
 #pragma unroll
                 for (int s = 0; s < 5; ++s)
                     a[s] = __builtin_bit_cast(
-                        half4_t, *(const u32x2 *)(lds + xoff<0>(ma, stride, 160u * bl + 40u * g + 8u * s)));
+                        half4_t, *(const u32x2 *)(lds + xoff<0>(ma, stride, 160u * bl + 40u * gm + 8u * s)));
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
-                    // pairs 0..4 from word 2g, 5..9 from word 2g + 1; step s takes pairs 2s, 2s + 1
+                    // pairs 0..4 from word 2gm, 5..9 from word 2gm + 1; step s takes pairs 2s, 2s + 1
                     const half2_t *u = t[r][0];
                     const half2_t *v = t[r][1];
                     float4_t D = __builtin_amdgcn_mfma_f32_16x16x16f16(
@@ -216,7 +255,7 @@ __device__ __forceinline__ void sm_tile(const SmProb &p, int row0, uint8_t *lds)
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
                     a[s] = __builtin_bit_cast(
-                        half8_t, *(const u32x4 *)(lds + xoff<1>(ma, stride, 128u * bl + 32u * g + 16u * s)));
+                        half8_t, *(const u32x4 *)(lds + xoff<1>(ma, stride, 128u * bl + 32u * gm + 16u * s)));
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
                     const half2_t *u = t[r][0];
@@ -267,7 +306,44 @@ __device__ __forceinline__ void sm_tile(const SmProb &p, int row0, uint8_t *lds)
         ++ic;
     };
 
-    if (nb >= 2 * U) {
+    if (kGrouped && nb >= 2 * S) {
+#pragma unroll
+        for (int u = 0; u < S; ++u) {
+            issue(u);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        int done = 0;
+        do {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                restage();
+#pragma unroll
+                for (int u = 0; u < U; ++u) consume(h * U + u);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < U; ++u) issue(h * U + u);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            done += S;
+        } while (done + 2 * S <= nb);
+        // slots hold blocks done .. done + S - 1; fewer than S are unissued
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            restage();
+#pragma unroll
+            for (int u = 0; u < U; ++u) consume(h * U + u);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (done + S + h * U + u < nb) issue(h * U + u);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            restage();
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (done + S + h * U + u < nb) consume(h * U + u);
+        }
+    } else if (nb >= 2 * U) {
         // Slots are issued in order, so that each slot's wait covers its own
         // loads only.
 #pragma unroll
@@ -306,26 +382,24 @@ __device__ __forceinline__ void sm_tile(const SmProb &p, int row0, uint8_t *lds)
     }
 
     if constexpr (MFMA) {
-        // lane (j, g) holds D[m = 4g + i][row j]; lanes g = 2, 3 hold the repeated rows
+        // lane (jm, gm) holds D[m = 4gm + i][row jm]; lanes gm = 2, 3 hold the repeated rows
 #pragma unroll
         for (int r = 0; r < 2; ++r)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int m = 4 * g + i, row = 16 * r + j;
-                if (g < 2 && m < M && row < valid) p.Y[p.ldy * m + row0 + row] = accm[r][i];
+                const int m = 4 * gm + i, row = 16 * r + jm;
+                if (gm < 2 && m < M && row < valid) p.Y[p.ldy * m + row0 + row] = accm[r][i];
             }
     } else {
-        // add the four lanes of each row; lane (j, g) stores m = g and g + 4
+        // add the four lanes (one quad) of each row; lane (j, g) stores m = g and g + 4
 #pragma unroll
         for (int r = 0; r < 2; ++r)
 #pragma unroll
             for (int m = 0; m < kMaxM; ++m) {
                 if (m < M) {
                     float v = accv[r][m];
-                    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-                    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-                    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-                    v = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+                    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, false));  // quad_perm 1032
+                    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4e, 0xf, 0xf, false));  // quad_perm 2301
                     const int row = 16 * r + j;
                     if ((m & 3) == g && row < valid) p.Y[p.ldy * m + row0 + row] = v;
                 }
@@ -440,7 +514,7 @@ int sm_wgs_per_cu(bool mfma, int lds)
 // chunking: the fewest chunks of whole blocks whose M staged rows fit the LDS
 // budget, equal in size up to U blocks (every boundary a multiple of U).
 pn_status sm_make(int t, const void *W, int64_t N, int64_t K, const void *X, int64_t ldx, int M, float *Y,
-                  int64_t ldy, SmProb &p)
+                  int64_t ldy, bool mfma, SmProb &p)
 {
     pn_status st = check_matrix(t, W, N, K);
     if (st) return st;
@@ -456,7 +530,7 @@ pn_status sm_make(int t, const void *W, int64_t N, int64_t K, const void *X, int
         cb = (nb + nchunks - 1) / nchunks;
         if (cb < nb) cb = (cb + kSmU - 1) / kSmU * kSmU;  // chunk boundaries at multiples of U blocks
         stride = (cb * bytes_per_block + 255) / 256 * 256;
-        if (stride * M <= kSmLdsMax) break;
+        if (stride * M <= (mfma ? kSmLdsMax : kSmLdsValu)) break;
         if (cb <= kSmU) return PN_EUNSUPPORTED;
     }
     memset(&p, 0, sizeof(p));
@@ -520,12 +594,12 @@ pn_status pn_gemm_smallm(pn_type t, const void *W, int64_t N, int64_t K, const v
 {
     SmArgs a;
     memset(&a, 0, sizeof(a));
-    pn_status st = sm_make(t, W, N, K, X, ldx, M, Y, ldy, a.p0);
+    const bool mfma = pn_get_smallm_math() == PN_SMALLM_MFMA;
+    pn_status st = sm_make(t, W, N, K, X, ldx, M, Y, ldy, mfma, a.p0);
     if (st) return st;
     const int64_t tiles = (N + kTileRows - 1) / kTileRows;
     a.count = 1;
     a.total_tiles = (int32_t)tiles;
-    const bool mfma = pn_get_smallm_math() == PN_SMALLM_MFMA;
     return sm_launch(a, sm_lds(a.p0), mfma, (hipStream_t)stream, mfma ? kVarSmallMMfma : kVarSmallMValu);
 }
 
@@ -538,9 +612,10 @@ pn_status pn_group_create_smallm(const pn_gemm_desc *descs, int count, pn_group 
     int lds = 0;
     int64_t tiles = 0;
     pn_status st = PN_OK;
+    const int math = pn_get_smallm_math();
     for (int i = 0; i < count && st == PN_OK; ++i) {
         const pn_gemm_desc &e = descs[i];
-        st = sm_make(e.type, e.W, e.N, e.K, e.X, e.ldx, e.M, e.Y, e.ldy, host[i]);
+        st = sm_make(e.type, e.W, e.N, e.K, e.X, e.ldx, e.M, e.Y, e.ldy, math == PN_SMALLM_MFMA, host[i]);
         if (st != PN_OK) break;
         host[i].tile0 = (int32_t)tiles;
         tiles += (e.N + kTileRows - 1) / kTileRows;
@@ -572,7 +647,7 @@ pn_status pn_group_create_smallm(const pn_gemm_desc *descs, int count, pn_group 
     g->count = count;
     g->total_tiles = (int)tiles;
     g->lds = lds;
-    g->flags = pn_get_smallm_math();
+    g->flags = math;
     *out = g;
     return PN_OK;
 }
