@@ -11,7 +11,7 @@ input, all inputs resident in HBM before timing starts.  Prints one JSON line.
 
 --config 4 runs the same sweep with M = 8 activation rows per matrix (the
 small-batch kernels; --math picks their arithmetic, the other one is timed
-beside it).
+beside it; --m 16 gives the k = 15 verification width).
 
 value = algorithmic bytes per token (packed weights + fp16 inputs + fp32
 outputs) / step time, in GB/s; tokens/s is reported beside it.
@@ -89,6 +89,7 @@ def main():
     ap.add_argument("--config", type=int, default=3, choices=[3, 4])
     ap.add_argument("--math", default="mfma", choices=["mfma", "valu"],
                     help="small-batch arithmetic (--config 4)")
+    ap.add_argument("--m", type=int, default=8, help="activation rows with --config 4 (1..16)")
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the other schedules")
@@ -120,7 +121,7 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: %d bytes read, %d written" % (n, n))
         del src, dst
-    m = None if args.config == 3 else 8
+    m = None if args.config == 3 else args.m
     schedule = args.schedule
     if m is not None and schedule == "layer":
         print("--config 4 runs the token and gemv schedules", file=sys.stderr)

@@ -1,11 +1,11 @@
-// pn_smallm.hip - small-batch PN GEMM (M <= 8 activation rows) for AMD
+// pn_smallm.hip - small-batch PN GEMM (M <= 16 activation rows) for AMD
 // Instinct MI355X (gfx950), and its C ABI: pn_gemm_smallm,
 // pn_group_create_smallm, pn_set_smallm_math.
 //
-// Y[m, r] = sum_k w[r, k] X[m, k] for m < M <= 8, the verification width of
-// speculative decoding (v100-skinny README, "How QPN works": an 8-row tile
-// costs the same whether or not every row carries work).  Each weight is
-// decoded once and used for all M rows.
+// Y[m, r] = sum_k w[r, k] X[m, k] for m < M <= 16, the verification width of
+// speculative decoding, M = k + 1 (v100-skinny README, "How QPN works": a
+// tile costs the same whether or not every row carries work, and k = 15 needs
+// 16 rows).  Each weight is decoded once and used for all M rows.
 //
 // Work layout.  A wave owns 32 consecutive rows (two groups of 16) and walks
 // their blocks in order, with a pipeline of U blocks of loads in flight.
@@ -16,8 +16,8 @@
 // Two maths over the same loads (pn_set_smallm_math):
 //   MFMA  the decoded weights of 16 rows x one block form the B operand of
 //         v_mfma_f32_16x16x16_f16 (pn3t: 5 steps per block) or
-//         v_mfma_f32_16x16x32_f16 (pn4t: 2 steps); X is the A operand, its
-//         rows 8..15 repeating rows 0..7 (their results are discarded).  Each
+//         v_mfma_f32_16x16x32_f16 (pn4t: 2 steps); X is the A operand (its 16
+//         rows are the batch; rows past M are discarded).  Each
 //         block starts a fresh accumulator, which is scaled by that block's d
 //         in fp32 and added to the running sum: folding d into fp16 operands
 //         would round.  The words and scale move to the operand layout (lane
@@ -75,7 +75,7 @@ constexpr int kWaveRows = 32;
 constexpr int kTileRows = kSmWaves * kWaveRows;
 constexpr int kSmLdsMax = PN_SM_LDS_KB * 1024;
 constexpr int kSmLdsValu = PN_SM_VALU_LDS_KB * 1024;
-constexpr int kMaxM = 8;
+constexpr int kMaxM = 16;  // the MFMA tile has 16 activation rows
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -106,13 +106,14 @@ struct SmArgs {
 
 // LDS address of byte o of staged activation row m.  Rows are `stride` bytes
 // apart (a multiple of 256).  The XOR moves 32-byte (pn3t) or 16-byte (pn4t)
-// pieces inside a 256-byte window so that the 32 distinct reads of one
-// operand load (8 rows x 4 lane groups) spread over the banks: pn3t reads 8
-// bytes at 40g + 8s, pn4t 16 bytes at 32g + 16s.
+// pieces inside a 256-byte window so that the distinct reads of one operand
+// load (up to 16 rows x 4 lane groups) spread over the banks as evenly as
+// their total size allows: pn3t reads 8 bytes at 40g + 8s, pn4t 16 bytes at
+// 32g + 16s.
 template <int TYPE>
 __device__ __forceinline__ uint32_t xoff(uint32_t m, uint32_t stride, uint32_t o)
 {
-    const uint32_t sw = TYPE == 0 ? (m << 5) : (((m & 1u) << 7) | ((m & 2u) << 3));
+    const uint32_t sw = TYPE == 0 ? ((m & 7u) << 5) : (((m & 1u) << 7) | ((m & 2u) << 3));
     return m * stride + (o ^ sw);
 }
 
@@ -165,7 +166,7 @@ __device__ __forceinline__ void sm_tile(const SmProb &p, int row0, uint8_t *lds)
                   valid > 0 ? (uint32_t)valid * (uint32_t)row_bytes : 0u);
     const int vs0 = j * row_bytes, vs1 = vs0 + 16 * row_bytes;  // block scale, rows j and 16 + j
     const int vw0 = vs0 + 2 + 8 * g, vw1 = vw0 + 16 * row_bytes;  // words 2g, 2g + 1
-    const uint32_t ma = (uint32_t)(jm & 7) < (uint32_t)M ? (uint32_t)(jm & 7) : 0u;  // A row (MFMA)
+    const uint32_t ma = jm < M ? (uint32_t)jm : 0u;  // A row (MFMA); rows >= M are discarded
 
     constexpr bool kGrouped = MFMA && PN_SM_GROUPED;
     constexpr int S = kGrouped ? 2 * U : U;  // load slots
@@ -382,16 +383,16 @@ __device__ __forceinline__ void sm_tile(const SmProb &p, int row0, uint8_t *lds)
     }
 
     if constexpr (MFMA) {
-        // lane (jm, gm) holds D[m = 4gm + i][row jm]; lanes gm = 2, 3 hold the repeated rows
+        // lane (jm, gm) holds D[m = 4gm + i][row jm]
 #pragma unroll
         for (int r = 0; r < 2; ++r)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = 4 * gm + i, row = 16 * r + jm;
-                if (gm < 2 && m < M && row < valid) p.Y[p.ldy * m + row0 + row] = accm[r][i];
+                if (m < M && row < valid) p.Y[p.ldy * m + row0 + row] = accm[r][i];
             }
     } else {
-        // add the four lanes (one quad) of each row; lane (j, g) stores m = g and g + 4
+        // add the four lanes (one quad) of each row; lane (j, g) stores m = g (mod 4)
 #pragma unroll
         for (int r = 0; r < 2; ++r)
 #pragma unroll

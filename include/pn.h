@@ -78,15 +78,15 @@ pn_status pn_gemv(pn_type t, const void *W, int64_t N, int64_t K,
 pn_status pn_gemv2(pn_type t, const void *W0, const void *W1, int64_t N,
                    int64_t K, const void *x, float *y0, float *y1, void *stream);
 
-/* Small-batch product for M <= 8 activation rows (speculative-decoding
- * verification width; v100-skinny README, "How QPN works"):
+/* Small-batch product for M <= 16 activation rows (speculative-decoding
+ * verification width M = k + 1; v100-skinny README, "How QPN works"):
  * Y[m*ldy + r] = sum_k w[r,k] * X[m*ldx + k] for m < M, r < N.
  * Each weight is decoded exactly once and used M times; products accumulate
  * in fp32, within 1e-5 * sum_k |w[r,k] X[m,k]| of the exact value.
  *   X : M rows of fp16, leading dimension ldx >= K (elements), 4-byte aligned,
  *       ldx even
  *   Y : M rows of fp32, leading dimension ldy >= N (elements), overwritten
- *   M : 1..8
+ *   M : 1..16
  * The arithmetic unit is the one pn_set_smallm_math selected. */
 pn_status pn_gemm_smallm(pn_type t, const void *W, int64_t N, int64_t K,
                          const void *X, int64_t ldx, int M,
@@ -97,7 +97,8 @@ pn_status pn_gemm_smallm(pn_type t, const void *W, int64_t N, int64_t K,
  *   PN_SMALLM_MFMA  decoded weights feed matrix-core products
  *                   (v_mfma_f32_16x16x16_f16 / 16x16x32_f16), one per block
  *                   and 16 rows, each scaled by its block's d in fp32; the
- *                   default (faster on MI355X at M = 8);
+ *                   default (faster on MI355X at M = 8: 3.0 vs 5.9 ms per
+ *                   64-layer token);
  *   PN_SMALLM_VALU  per-lane fp16 dot products (v_dot2_f32_f16) reduced
  *                   across the lanes of a row.
  * The setting is process-wide and read when a call is made or a group is
@@ -150,7 +151,7 @@ typedef struct pn_gemm_desc {
     int64_t ldx;     /* elements, >= K, even                    */
     int64_t ldy;     /* elements, >= N                          */
     int32_t type;    /* pn_type                                 */
-    int32_t M;       /* 1..8                                    */
+    int32_t M;       /* 1..16                                   */
 } pn_gemm_desc;
 
 pn_status pn_group_create_smallm(const pn_gemm_desc *descs, int count, pn_group **out);

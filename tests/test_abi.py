@@ -67,7 +67,7 @@ def test_gemv_host_checks(args, status):
 def test_other_entry_points_host_checks():
     assert B.pn_gemv2("pn3t", FAKE, None, 4, 80, FAKE, FAKE, FAKE, stream=0, check=False) == PN_EINVAL
     assert B.pn_gemv2("pn4t", FAKE, FAKE, 4, 80, FAKE, FAKE, FAKE, stream=0, check=False) == PN_ESHAPE
-    assert B.pn_gemm_smallm("pn3t", FAKE, 4, 80, FAKE, 80, 9, FAKE, 4, stream=0, check=False) == PN_ESHAPE
+    assert B.pn_gemm_smallm("pn3t", FAKE, 4, 80, FAKE, 80, 17, FAKE, 4, stream=0, check=False) == PN_ESHAPE
     assert B.pn_gemm_smallm("pn3t", FAKE, 4, 80, FAKE, 80, 0, FAKE, 4, stream=0, check=False) == PN_ESHAPE
     assert B.pn_gemm_smallm("pn3t", FAKE, 4, 80, FAKE, 79, 2, FAKE, 4, stream=0, check=False) == PN_ESHAPE
     assert B.pn_gemm_smallm("pn3t", FAKE, 4, 80, FAKE, 81, 2, FAKE, 4, stream=0, check=False) == PN_ESHAPE
@@ -98,7 +98,7 @@ def test_group_host_checks():
 def test_smallm_group_host_checks():
     ok = ("pn3t", FAKE, 4, 80, FAKE, 80, 2, FAKE, 4)
     bad = [
-        (("pn3t", FAKE, 4, 80, FAKE, 80, 9, FAKE, 4), PN_ESHAPE),      # M > 8
+        (("pn3t", FAKE, 4, 80, FAKE, 80, 17, FAKE, 4), PN_ESHAPE),     # M > 16
         (("pn3t", FAKE, 4, 80, FAKE, 81, 2, FAKE, 4), PN_ESHAPE),      # odd ldx
         (("pn4t", FAKE, 4, 80, FAKE, 80, 2, FAKE, 4), PN_ESHAPE),      # K not whole pn4t blocks
         (("pn3t", FAKE, 4, 80, FAKE + 2, 80, 2, FAKE, 4), PN_EALIGN),  # X

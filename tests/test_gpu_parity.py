@@ -258,7 +258,7 @@ def gpu_smallm(t, w, n, k, X, m, ldx, ldy):
 
 @pytest.mark.parametrize("smallm_math", MATHS, indirect=True)
 @pytest.mark.parametrize("t,n,k", SMALLM_SHAPES)
-@pytest.mark.parametrize("m", [1, 2, 5, 8])
+@pytest.mark.parametrize("m", [1, 2, 5, 8, 9, 16])
 def test_gemm_smallm(smallm_math, t, n, k, m):
     w, g = random_matrix(n + k + m, t, n, k)
     ldx, ldy = k + 2 * (m % 2), n + 3
@@ -281,16 +281,18 @@ def test_gemm_smallm(smallm_math, t, n, k, m):
 def test_smallm_one_hot_exact(smallm_math, t):
     """Row m of X is one-hot at k_m: Y[m, r] = w[r, k_m] exactly (one exact
     product, the rest zeros).  Pins the k <-> (block, word, slot) map of the
-    operand layouts, including both words of a lane and the block edges."""
+    operand layouts, including both words of a lane, the block edges and all
+    16 batch rows."""
     wpb = WPB[t]
     n, k = 70, wpb * 6
     w, _ = random_matrix(17, t, n, k)
-    ks = [0, 1, wpb // 4 - 1, wpb // 4, wpb // 2 + 3, wpb - 1, wpb, 5 * wpb + wpb - 2]
-    X = np.zeros((8, k), np.float16)
+    ks = [0, 1, wpb // 4 - 1, wpb // 4, wpb // 2 + 3, wpb - 1, wpb, 5 * wpb + wpb - 2,
+          2, wpb // 8, wpb // 4 + 7, wpb // 2 - 1, wpb // 2, 3 * wpb // 4, 2 * wpb + 9, 4 * wpb - 1]
+    X = np.zeros((16, k), np.float16)
     for m, km in enumerate(ks):
         X[m, km] = 1.0
     say("smallm one-hot %s %s" % (smallm_math, t))
-    Y = gpu_smallm(t, w, n, k, X, 8, k, n)
+    Y = gpu_smallm(t, w, n, k, X, 16, k, n)
     dense = pnref.dequantize(t, w, n, k)
     for m, km in enumerate(ks):
         assert_bits_equal(Y[m] + 0.0, dense[:, km] + 0.0, "one-hot m=%d k=%d" % (m, km))
@@ -312,7 +314,7 @@ def test_smallm_group(smallm_math):
     """One launch over problems of mixed type, shape, M and leading
     dimensions; each against the oracle."""
     specs = [("pn3t", 100, 5120, 8), ("pn4t", 70, 17408, 3), ("pn4t", 300, 6144, 8),
-             ("pn3t", 5, 80, 1), ("pn4t", 260, 5120, 8), ("pn3t", 33, 80 * 9, 6)]
+             ("pn3t", 5, 80, 1), ("pn4t", 260, 5120, 16), ("pn3t", 33, 80 * 9, 6), ("pn3t", 64, 5120, 13)]
     host, probs, keep = [], [], []
     for i, (t, n, k, m) in enumerate(specs):
         w, g = random_matrix(1000 + i, t, n, k)
