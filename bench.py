@@ -28,8 +28,14 @@ sys.path.insert(0, ROOT)
 
 METRIC = "PN GEMV achieved HBM GB/s (% of peak) + 27B-shaped layer-sweep tokens/s"
 PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
-KERNEL_SOURCES = ["bit_quantized_decode_pn3t_amd/csrc/pn_kernels.hip",
-                  "bit_quantized_decode_pn3t_amd/csrc/pn_device.h"]
+# Sources of the kernel each workload times (M = 1: gemv_stream; M > 1:
+# gemm_stream): the committed counters are valid for one hash of these.
+KERNEL_SOURCES = {
+    "m1": ["bit_quantized_decode_pn3t_amd/csrc/pn_kernels.hip",
+           "bit_quantized_decode_pn3t_amd/csrc/pn_device.h"],
+    "smallm": ["bit_quantized_decode_pn3t_amd/csrc/pn_smallm.hip",
+               "bit_quantized_decode_pn3t_amd/csrc/pn_device.h"],
+}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -37,15 +43,15 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-def kernel_hash():
+def kernel_hash(kind):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, kind):
     """HBM bytes per launch from committed rocprofv3 counters, if they were
     taken on the current kernel source; else None."""
     try:
@@ -54,7 +60,7 @@ def measured_traffic(workload):
     except (OSError, ValueError):
         return None
     e = t.get(workload)
-    if not e or e.get("kernel_hash") != kernel_hash():
+    if not e or e.get("kernel_hash") != kernel_hash(kind):
         return None
     return e.get("bytes_per_launch")
 
@@ -177,18 +183,19 @@ def main():
     tok_s = args.steps / wall
 
     workload = "sweep64_m1_%s" % schedule if m is None else "sweep64_m%d_%s_%s" % (m, schedule, args.math)
+    kind = "m1" if m is None else "smallm"
     if schedule == "token":
         # one launch per step: the events bracket exactly the dominant kernel
         kern_ms = sum(ev_ms) / len(ev_ms)
         achieved = bytes_per_token / (kern_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(achieved / PEAK_GBPS, 4), "traffic": measured_traffic(workload),
+                    "frac": round(achieved / PEAK_GBPS, 4), "traffic": measured_traffic(workload, kind),
                     "kernel": "gemv_stream" if m is None else "gemm_stream<%s>" % args.math,
                     "variant": variant, "kernel_avg_ms": round(kern_ms, 4),
                     "algorithmic_bytes_per_launch": bytes_per_token}
     else:
         roofline = {"bound": "hbm", "achieved": round(value, 1), "peak": PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(value / PEAK_GBPS, 4), "traffic": measured_traffic(workload),
+                    "frac": round(value / PEAK_GBPS, 4), "traffic": measured_traffic(workload, kind),
                     "kernel": variant, "note": "step wall time over %d launches" % sw.launches(schedule)}
 
     launches = sw.launches(schedule)
@@ -271,7 +278,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "other_schedules": secondary,
-        "kernel_hash": kernel_hash(),
+        "kernel_hash": kernel_hash(kind),
     }
     print(json.dumps(out), flush=True)
 
