@@ -65,6 +65,87 @@ def measured_traffic(workload, kind):
     return e.get("bytes_per_launch")
 
 
+def per_config_timing(B, synth, torch):
+    """Workloads 0-2 one call at a time: HIP events around every call, >= 50
+    timed calls after 10 warm-up calls, rotating weight copies so that
+    workloads 1 and 2 come from HBM rather than the 256 MB last-level cache.
+    Workload 2's codes are random bytes of its shape: its quantized weights
+    come from the oracle, and the bytes moved are the same."""
+    import numpy as np
+
+    def stats(ms, nbytes):
+        a = np.sort(np.array(ms))
+        q = lambda f: float(a[min(len(a) - 1, int(f * len(a)))])
+        return {"us_p10": round(q(0.1) * 1e3, 2), "us_p50": round(q(0.5) * 1e3, 2),
+                "us_p90": round(q(0.9) * 1e3, 2), "gbps_p50": round(nbytes / (q(0.5) * 1e-3) / 1e9, 1),
+                "bytes_per_call": nbytes, "calls": len(ms)}
+
+    def timed(fn, copies, calls=60, warm=10):
+        for i in range(warm):
+            fn(i % copies)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+        for i, (a, b) in enumerate(ev):
+            a.record()
+            fn(i % copies)
+            b.record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+    out = {}
+    dev = torch.device("cuda")
+    c0 = synth.config0()
+    w0 = torch.from_numpy(c0["W"]).to(dev)
+    x0 = torch.from_numpy(c0["x"]).to(dev)
+    y0 = torch.empty(c0["N"], dtype=torch.float32, device=dev)
+    ms = timed(lambda i: B.pn_gemv("pn3t", w0, 256, 5120, x0, y0), 1, calls=200)
+    out["workload0_pn3t_256x5120"] = dict(stats(ms, c0["W"].nbytes + 5120 * 2 + 256 * 4),
+                                          note="L2-resident: a latency, not an HBM rate")
+    c1 = synth.config1()
+    w1 = [torch.from_numpy(c1["W"]).to(dev) for _ in range(8)]
+    x1 = torch.from_numpy(c1["x"]).to(dev)
+    y1 = torch.empty(c1["N"], dtype=torch.float32, device=dev)
+    ms = timed(lambda i: B.pn_gemv("pn4t", w1[i], 5120, 17408, x1, y1), 8)
+    out["workload1_pn4t_5120x17408"] = dict(stats(ms, c1["W"].nbytes + 17408 * 2 + 5120 * 4), copies=8)
+    del w1
+    g = synth.rng(2, 0, 3)
+    wg = [torch.from_numpy(synth.random_blocks(g, "pn3t", 17408, 5120)).to(dev) for _ in range(4)]
+    wu = [torch.from_numpy(synth.random_blocks(g, "pn3t", 17408, 5120)).to(dev) for _ in range(4)]
+    x2 = torch.from_numpy(synth.activation(g, 5120)).to(dev)
+    yg = torch.empty(17408, dtype=torch.float32, device=dev)
+    yu = torch.empty(17408, dtype=torch.float32, device=dev)
+    ms = timed(lambda i: B.pn_gemv2("pn3t", wg[i], wu[i], 17408, 5120, x2, yg, yu), 4)
+    out["workload2_gate_up_2x17408x5120"] = dict(stats(ms, 2 * wg[0].numel() + 5120 * 2 + 2 * 17408 * 4),
+                                                 copies=4, codes="random bytes of the shape")
+    del wg, wu
+    torch.cuda.empty_cache()
+    return out
+
+
+def host_read_gbps():
+    """Host memory read rate (numpy sum over 1 GiB of uint64, best of 3)."""
+    import numpy as np
+    a = np.ones(1 << 27, dtype=np.uint64)
+    best = None
+    for _ in range(3):
+        t0 = time.perf_counter()
+        a.sum()
+        dt = time.perf_counter() - t0
+        best = dt if best is None or dt < best else best
+    return round(a.nbytes / best / 1e9, 2)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(layers, threads, m=None):
     """The oracle (fp64 decode + GEMV, C, OpenMP over rows) on a bounded
     sample of the sweep: the first `layers` layers, scaled to one token."""
@@ -101,6 +182,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="skip the other schedules")
     ap.add_argument("--cpu-layers", type=int, default=None,
                     help="layers in the oracle's sample (default 64 at M=1, 8 at M=8)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the one-call timings of workloads 0-2")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run one device copy of this many MiB (a kernel of known traffic "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -239,6 +322,11 @@ def main():
     torch.cuda.empty_cache()
     log("read ceiling %.1f GB/s" % read_ceiling)
 
+    per_config = None
+    if not args.no_configs and m is None:
+        log("one-call timings of workloads 0-2")
+        per_config = per_config_timing(B, synth, torch)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu_layers = args.cpu_layers or (64 if m is None else 8)
@@ -250,8 +338,13 @@ def main():
                "sample": "first %d of %d layers (%.2f GB packed, %.1f%% of a token) in %.2f s; "
                          "fp64 decode+%s, OpenMP over rows" % (cpu_layers, args.layers, sample_bytes / 1e9,
                                                               100 * token_fraction, dt,
-                                                              "GEMV" if m is None else "GEMM (M=8)"),
-               "gbps_packed": round(sample_bytes / dt / 1e9, 3)}
+                                                              "GEMV" if m is None else "GEMM (M=%d)" % m),
+               "gbps_packed": round(sample_bytes / dt / 1e9, 3),
+               "cpu_model": cpu_model(), "host_read_gbps": host_read_gbps()}
+        one_layers = max(1, cpu_layers // 8)
+        dt1, bytes1, _ = cpu_baseline(one_layers, 1, m)
+        cpu["one_thread"] = {"value": round(bytes1 / weights_per_token / dt1, 4), "unit": "tok/s",
+                             "sample": "first %d layers in %.2f s" % (one_layers, dt1)}
 
     out = {
         "metric": METRIC,
@@ -278,6 +371,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "other_schedules": secondary,
+        "per_config": per_config,
         "kernel_hash": kernel_hash(kind),
     }
     print(json.dumps(out), flush=True)
