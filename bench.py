@@ -28,10 +28,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = "PN GEMV achieved HBM GB/s (% of peak) + 27B-shaped layer-sweep tokens/s"
 PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
-# Sources of the kernel each workload times (M = 1: gemv_stream; M > 1:
-# gemm_stream): the committed counters are valid for one hash of these.
+# Sources of the kernel each workload times (M = 1: gemv_rows for the
+# one-launch sweep, gemv_stream for smaller launches; M > 1: gemm_stream):
+# the committed counters are valid for one hash of these.
 KERNEL_SOURCES = {
     "m1": ["bit_quantized_decode_pn3t_amd/csrc/pn_kernels.hip",
+           "bit_quantized_decode_pn3t_amd/csrc/pn_gemv_rows.hip",
            "bit_quantized_decode_pn3t_amd/csrc/pn_device.h"],
     "smallm": ["bit_quantized_decode_pn3t_amd/csrc/pn_smallm.hip",
                "bit_quantized_decode_pn3t_amd/csrc/pn_device.h"],
@@ -273,7 +275,7 @@ def main():
         achieved = bytes_per_token / (kern_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / PEAK_GBPS, 4), "traffic": measured_traffic(workload, kind),
-                    "kernel": "gemv_stream" if m is None else "gemm_stream<%s>" % args.math,
+                    "kernel": variant.replace("_group", "") if m is None else "gemm_stream<%s>" % args.math,
                     "variant": variant, "kernel_avg_ms": round(kern_ms, 4),
                     "algorithmic_bytes_per_launch": bytes_per_token}
     else:

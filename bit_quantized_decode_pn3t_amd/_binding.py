@@ -16,6 +16,7 @@ PN_PN4T = 1
 TYPES = {"pn3t": PN_PN3T, "pn4t": PN_PN4T, PN_PN3T: PN_PN3T, PN_PN4T: PN_PN4T}
 
 SMALLM_MATH = {"mfma": 0, "valu": 1, 0: 0, 1: 1}
+GEMV_KERNEL = {"auto": 0, "stream": 1, "rows": 2, 0: 0, 1: 1, 2: 2}
 
 STATUS = {0: "PN_OK", -1: "PN_EINVAL", -2: "PN_ESHAPE", -3: "PN_EALIGN",
           -4: "PN_EUNSUPPORTED", -5: "PN_ELAUNCH", -6: "PN_ENOMEM"}
@@ -24,7 +25,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpn.so")
 
 # Every symbol include/pn.h declares.
 EXPORTS = ("pn_weights_per_block", "pn_row_bytes", "pn_gemv", "pn_gemv2",
-           "pn_gemm_smallm", "pn_set_smallm_math", "pn_get_smallm_math", "pn_dequantize",
+           "pn_gemm_smallm", "pn_set_smallm_math", "pn_get_smallm_math", "pn_set_gemv_kernel",
+           "pn_get_gemv_kernel", "pn_dequantize",
            "pn_group_create", "pn_group_create_smallm", "pn_group_run", "pn_group_destroy",
            "pn_read_probe_scratch_bytes", "pn_read_probe", "pn_status_str", "pn_last_variant",
            "pn_variant_name")
@@ -72,6 +74,10 @@ def lib():
     L.pn_gemv2.restype = i32
     L.pn_gemm_smallm.argtypes = [i32, vp, i64, i64, vp, i64, i32, vp, i64, vp]
     L.pn_gemm_smallm.restype = i32
+    L.pn_set_gemv_kernel.argtypes = [i32]
+    L.pn_set_gemv_kernel.restype = i32
+    L.pn_get_gemv_kernel.argtypes = []
+    L.pn_get_gemv_kernel.restype = i32
     L.pn_set_smallm_math.argtypes = [i32]
     L.pn_set_smallm_math.restype = i32
     L.pn_get_smallm_math.argtypes = []
@@ -171,6 +177,19 @@ def pn_set_smallm_math(math, check=True):
 
 def pn_get_smallm_math():
     return {0: "mfma", 1: "valu"}[lib().pn_get_smallm_math()]
+
+
+def pn_set_gemv_kernel(kernel, check=True):
+    """Select the M = 1 kernel: "auto" (row tiles for large launches),
+    "stream" (register pipeline) or "rows" (row tiles wherever they apply)."""
+    st = lib().pn_set_gemv_kernel(GEMV_KERNEL.get(kernel, kernel if isinstance(kernel, int) else -1))
+    if check:
+        _check(st, "pn_set_gemv_kernel")
+    return st
+
+
+def pn_get_gemv_kernel():
+    return {0: "auto", 1: "stream", 2: "rows"}[lib().pn_get_gemv_kernel()]
 
 
 def pn_dequantize(pn_type, W, N, K, out, stream=None, check=True):

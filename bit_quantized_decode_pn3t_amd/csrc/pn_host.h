@@ -22,6 +22,8 @@ enum Variant {
     kVarSmallMMfma = 6,
     kVarGroupSmallMValu = 7,
     kVarGroupSmallMMfma = 8,
+    kVarRows = 9,
+    kVarGroupRows = 10,
 };
 
 extern thread_local int g_last_variant;
@@ -43,7 +45,7 @@ inline pn_status check_matrix(int t, const void *W, int64_t N, int64_t K)
 // Compute units of the current device (256 if the query fails).
 int device_cus();
 
-enum GroupKind { kGroupGemv = 0, kGroupSmallM = 1 };
+enum GroupKind { kGroupGemv = 0, kGroupSmallM = 1, kGroupGemvRows = 2 };
 
 }  // namespace host
 }  // namespace pn
@@ -53,7 +55,7 @@ struct pn_group {
     int kind;           // pn::host::GroupKind
     void *table;        // device copy of the per-problem records
     int count;
-    int total_tiles;
+    int total_tiles;    // tiles (gemv_stream, gemm_stream) or waves (gemv_rows)
     int lds;            // dynamic LDS bytes of the launch
     int flags;          // kind-specific launch choice
 };
@@ -62,5 +64,15 @@ namespace pn {
 namespace host {
 // Launch a small-M group plan (pn_smallm.hip).
 pn_status smallm_group_run(const pn_group *g, hipStream_t s);
+// The row-tile M = 1 kernel (pn_gemv_rows.hip): whether it takes a problem,
+// whether a launch of that many 16-row tiles is large enough for it, and
+// its launches.
+bool rows_ok(int t, const void *W, int64_t K, const void *x);
+bool rows_pays(int64_t tiles);
+int64_t rows_tiles(int64_t N);
+pn_status rows_launch(int t, const void *W0, const void *W1, int64_t N, int64_t K, const void *x, float *y0,
+                      float *y1, hipStream_t s);
+pn_status rows_group_create(const pn_gemv_desc *descs, int count, pn_group **out);
+pn_status rows_group_run(const pn_group *g, hipStream_t s);
 }  // namespace host
 }  // namespace pn

@@ -86,25 +86,43 @@ struct StreamArgs {
 // to a 4-byte entry in a second array (one ds_read_b128 + one ds_read_b32,
 // both aligned).  LDS bytes: 16*nw (+ 4*nw for pn3t) = 2*K.
 // ---------------------------------------------------------------------------
-template <int V>
+// Threads walk LDS entries in order (conflict-free stores); entry e of slot
+// v holds word f = V * (e - v * per) + v.  Each thread issues the loads of up
+// to kStageBatch entries before it writes any of them: a loop that waited
+// for every entry's load before the next took one memory round trip per
+// kThreads entries, microseconds per problem for the long rows.  Buffer
+// loads (not global ones) keep the compiler's wait analysis of the weight
+// pipeline exact; entries past the end read zeros and are not written.
+constexpr int kStageBatch = 8;
+
+template <int TYPE, int V>
 __device__ __forceinline__ void stage_x(const Prob &p, uint8_t *lds)
 {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int kEntry = TYPE == 0 ? 20 : 16;  // activation bytes per word
     const int nw = p.nw;
     const int per = nw / V;  // entries per slot
-    uint4 *a = (uint4 *)lds;
+    u32x4 *a = (u32x4 *)lds;
     uint32_t *b = (uint32_t *)(lds + 16 * nw);
-    // Threads walk LDS entries in order (conflict-free stores); entry e of
-    // slot v holds word f = V * (e - v * per) + v.
-    for (int e = threadIdx.x; e < nw; e += kThreads) {
-        const int v = e / per;
-        const int f = V * (e - v * per) + v;
-        if (p.type == 0) {
-            const uint8_t *src = p.x + 20 * (size_t)f;
-            a[e] = make_uint4(load_u32(src), load_u32(src + 4), load_u32(src + 8), load_u32(src + 12));
-            b[e] = load_u32(src + 16);
-        } else {
-            const uint8_t *src = p.x + 16 * (size_t)f;
-            a[e] = make_uint4(load_u32(src), load_u32(src + 4), load_u32(src + 8), load_u32(src + 12));
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(uniform_ptr(p.x), (uint32_t)(kEntry * nw));
+    for (int e0 = 0; e0 < nw; e0 += kStageBatch * kThreads) {
+        u32x4 va[kStageBatch];
+        uint32_t vb[kStageBatch];
+#pragma unroll
+        for (int k = 0; k < kStageBatch; ++k) {
+            const int e = e0 + k * kThreads + (int)threadIdx.x;
+            const int v = e / per;
+            const int off = kEntry * (V * (e - v * per) + v);
+            va[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+            if constexpr (TYPE == 0) vb[k] = __builtin_amdgcn_raw_buffer_load_b32(xr, off + 16, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < kStageBatch; ++k) {
+            const int e = e0 + k * kThreads + (int)threadIdx.x;
+            if (e < nw) {
+                a[e] = va[k];
+                if constexpr (TYPE == 0) b[e] = vb[k];
+            }
         }
     }
 }
@@ -306,7 +324,10 @@ __global__ __launch_bounds__(kThreads) void gemv_stream(StreamArgs args)
             p.rpw = uniform(c.rpw);
             next0 = uniform(problem_tile0(args, i + 1));
             __syncthreads();
-            stage_x<V>(p, lds);
+            if (p.type == 0)
+                stage_x<0, V>(p, lds);
+            else
+                stage_x<1, V>(p, lds);
             __syncthreads();
         }
         const int row0 = ((tile - p.tile0) * kWaves + wave) * p.rpw;
@@ -541,8 +562,9 @@ pn_status pn_gemv(pn_type t, const void *W, int64_t N, int64_t K, const void *x,
     if (st) return st;
     if (!x || !y) return PN_EINVAL;
     if (!aligned4(x) || !aligned4(y)) return PN_EALIGN;
-    Prob p = make_prob(t, W, N, K, x, y);
     hipStream_t s = (hipStream_t)stream;
+    if (rows_ok(t, W, K, x) && rows_pays(rows_tiles(N))) return rows_launch(t, W, nullptr, N, K, x, y, nullptr, s);
+    Prob p = make_prob(t, W, N, K, x, y);
     if (!stream_ok(p)) return launch_generic(p, p, 1, s);
     const int lds = lds_bytes_for(p);
     const int64_t tiles = plan_tiles(&p, 1, lds);
@@ -565,9 +587,11 @@ pn_status pn_gemv2(pn_type t, const void *W0, const void *W1, int64_t N, int64_t
     if (st) return st;
     if (!x || !y0 || !y1) return PN_EINVAL;
     if (!aligned4(x) || !aligned4(y0) || !aligned4(y1)) return PN_EALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    if (rows_ok(t, W0, K, x) && rows_ok(t, W1, K, x) && rows_pays(2 * rows_tiles(N)))
+        return rows_launch(t, W0, W1, N, K, x, y0, y1, s);
     Prob p0 = make_prob(t, W0, N, K, x, y0);
     Prob p1 = make_prob(t, W1, N, K, x, y1);
-    hipStream_t s = (hipStream_t)stream;
     if (!stream_ok(p0)) return launch_generic(p0, p1, 2, s);
     const int lds = lds_bytes_for(p0);
     Prob pp[2] = {p0, p1};
@@ -610,15 +634,28 @@ pn_status pn_group_create(const pn_gemv_desc *descs, int count, pn_group **out)
     int lds = 0;
     bool v2 = true;
     pn_status st = PN_OK;
+    bool all_rows = true;
+    int64_t rows_total = 0;
     for (int i = 0; i < count && st == PN_OK; ++i) {
         const pn_gemv_desc &e = descs[i];
         st = check_matrix(e.type, e.W, e.N, e.K);
         if (st == PN_OK && (!e.x || !e.y)) st = PN_EINVAL;
         if (st == PN_OK && (!aligned4(e.x) || !aligned4(e.y))) st = PN_EALIGN;
         if (st == PN_OK) {
-            host[i] = make_prob(e.type, e.W, e.N, e.K, e.x, e.y);
-            if (!stream_ok(host[i])) st = PN_EUNSUPPORTED;
+            all_rows = all_rows && rows_ok(e.type, e.W, e.K, e.x);
+            rows_total += rows_tiles(e.N);
         }
+    }
+    // the row-tile kernel takes the group if it takes every problem and the
+    // launch is large enough
+    if (st == PN_OK && all_rows && rows_pays(rows_total)) {
+        free(host);
+        return rows_group_create(descs, count, out);
+    }
+    for (int i = 0; i < count && st == PN_OK; ++i) {
+        const pn_gemv_desc &e = descs[i];
+        host[i] = make_prob(e.type, e.W, e.N, e.K, e.x, e.y);
+        if (!stream_ok(host[i])) st = PN_EUNSUPPORTED;
         if (st == PN_OK) {
             v2 = v2 && stream_v2(host[i]);
             if (lds_bytes_for(host[i]) > lds) lds = lds_bytes_for(host[i]);
@@ -660,6 +697,7 @@ pn_status pn_group_run(const pn_group *g, void *stream)
 {
     if (!g) return PN_EINVAL;
     if (g->kind == kGroupSmallM) return smallm_group_run(g, (hipStream_t)stream);
+    if (g->kind == kGroupGemvRows) return rows_group_run(g, (hipStream_t)stream);
     StreamArgs a;
     memset(&a, 0, sizeof(a));
     a.table = (const Prob *)g->table;
@@ -702,6 +740,8 @@ const char *pn_variant_name(int v)
     case kVarSmallMMfma: return "gemm_stream_mfma";
     case kVarGroupSmallMValu: return "gemm_stream_valu_group";
     case kVarGroupSmallMMfma: return "gemm_stream_mfma_group";
+    case kVarRows: return "gemv_rows";
+    case kVarGroupRows: return "gemv_rows_group";
     case kVarDequant: return "dequant";
     case kVarGroupStream: return "gemv_stream_group";
     }

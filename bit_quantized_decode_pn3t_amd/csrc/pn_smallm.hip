@@ -120,7 +120,8 @@ __device__ __forceinline__ uint32_t xoff(uint32_t m, uint32_t stride, uint32_t o
 // Stage activation blocks [b0, b0 + nbc) of all M rows into LDS.  The loads
 // are buffer loads like the weight loads: mixing in global (FLAT-family)
 // loads makes the compiler's wait analysis drain every load in flight at the
-// pipeline's loop head.
+// pipeline's loop head.  Each thread issues up to kStageBatch loads before it
+// writes any of them (one memory round trip per batch, not per piece).
 template <int TYPE>
 __device__ __forceinline__ void stage_chunk(const SmProb &p, int b0, int nbc, uint8_t *lds)
 {
@@ -130,10 +131,22 @@ __device__ __forceinline__ void stage_chunk(const SmProb &p, int b0, int nbc, ui
     const int row_stride = (int)(2 * p.ldx);
     const __amdgpu_buffer_rsrc_t xr =
         make_rsrc(uniform_ptr(p.X + (size_t)2 * b0 * W), (uint32_t)(row_stride * (p.M - 1) + 16 * per_row));
-    for (int i = threadIdx.x; i < total; i += kSmThreads) {
-        const int m = i / per_row, q = i - m * per_row;
-        const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, row_stride * m + 16 * q, 0, 0));
-        *(u32x4 *)(lds + xoff<TYPE>((uint32_t)m, (uint32_t)p.stride, 16u * q)) = v;
+    constexpr int kStageBatch = 4;
+    for (int i0 = 0; i0 < total; i0 += kStageBatch * kSmThreads) {
+        u32x4 v[kStageBatch];
+#pragma unroll
+        for (int k = 0; k < kStageBatch; ++k) {
+            const int i = i0 + k * kSmThreads + (int)threadIdx.x;
+            const int m = i / per_row, q = i - m * per_row;
+            // pieces past the end read zeros (offset past the resource) and are not written
+            v[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, row_stride * m + 16 * q, 0, 0));
+        }
+#pragma unroll
+        for (int k = 0; k < kStageBatch; ++k) {
+            const int i = i0 + k * kSmThreads + (int)threadIdx.x;
+            const int m = i / per_row, q = i - m * per_row;
+            if (i < total) *(u32x4 *)(lds + xoff<TYPE>((uint32_t)m, (uint32_t)p.stride, 16u * q)) = v[k];
+        }
     }
 }
 

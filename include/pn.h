@@ -108,6 +108,24 @@ typedef enum { PN_SMALLM_MFMA = 0, PN_SMALLM_VALU = 1 } pn_smallm_math;
 pn_status pn_set_smallm_math(pn_smallm_math m);
 pn_smallm_math pn_get_smallm_math(void);
 
+/* Which kernel runs the M = 1 products (pn_gemv, pn_gemv2 and pn_group_*):
+ *   PN_GEMV_AUTO    the row-tile kernel where it applies and the launch is
+ *                   large enough, else the register-pipeline kernel; the
+ *                   default.  The row-tile kernel applies to rows of whole
+ *                   8-block periods (K a multiple of 640 for pn3t, 512 for
+ *                   pn4t) with 16-byte-aligned W and x; "large enough" is at
+ *                   least 8 sixteen-row tiles per wave of the device (8192
+ *                   tiles, 131,072 rows, on a 256-CU MI355X), because it
+ *                   balances its work in whole tiles;
+ *   PN_GEMV_STREAM  always the register-pipeline kernel;
+ *   PN_GEMV_ROWS    the row-tile kernel wherever it applies, whatever the
+ *                   launch size.
+ * All meet the same accuracy bar.  Process-wide; read when a call is made or
+ * a group is created.  Returns PN_EINVAL for an unknown value. */
+typedef enum { PN_GEMV_AUTO = 0, PN_GEMV_STREAM = 1, PN_GEMV_ROWS = 2 } pn_gemv_kernel;
+pn_status pn_set_gemv_kernel(pn_gemv_kernel k);
+pn_gemv_kernel pn_get_gemv_kernel(void);
+
 /* Dense fp32 copy of the decoded weights, out[r*K + k] = d * (n - z),
  * bit-exact with the format's definition ("Exact decode in fp32": no
  * rounding in decode, so every correct decoder gives the same bits).
@@ -134,9 +152,13 @@ typedef struct pn_group pn_group;
  * call allocates device memory for the plan's tables and copies them there
  * synchronously; the plan holds the descriptors' device pointers, which must
  * stay valid while the plan is used.  Returns PN_ENOMEM if allocation fails.
- * Every problem's rows must be whole groups of 8 blocks (K a multiple of 640
- * for pn3t, 512 for pn4t) with 2*K <= 64 KiB of activation; other shapes
- * return PN_EUNSUPPORTED (pn_gemv takes them one at a time). */
+ * The plan runs on the row-tile kernel if that takes every problem and the
+ * launch (see pn_set_gemv_kernel); otherwise every problem's rows must be
+ * whole groups of 8 blocks (K a multiple of 640 for pn3t, 512 for pn4t) with
+ * 2*K <= 64 KiB of activation, and other shapes return PN_EUNSUPPORTED
+ * (pn_gemv takes them one at a time).  The kernel choice is made here, once,
+ * for the device current at this call; running the plan on a device with a
+ * different number of compute units returns PN_EUNSUPPORTED. */
 pn_status pn_group_create(const pn_gemv_desc *descs, int count, pn_group **out);
 
 /* The small-batch counterpart: each entry is one pn_gemm_smallm problem

@@ -121,3 +121,15 @@ def test_smallm_math_setting():
     assert B.pn_get_smallm_math() == "valu"
     B.pn_set_smallm_math("mfma")
     assert B.pn_get_smallm_math() == "mfma"
+
+
+def test_gemv_kernel_setting():
+    assert B.pn_get_gemv_kernel() == "auto"
+    assert B.pn_set_gemv_kernel(5, check=False) == PN_EINVAL
+    assert B.pn_get_gemv_kernel() == "auto"
+    B.pn_set_gemv_kernel("stream")
+    assert B.pn_get_gemv_kernel() == "stream"
+    B.pn_set_gemv_kernel("rows")
+    assert B.pn_get_gemv_kernel() == "rows"
+    B.pn_set_gemv_kernel("auto")
+    assert B.pn_get_gemv_kernel() == "auto"

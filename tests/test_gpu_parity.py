@@ -94,27 +94,65 @@ def test_dequant_shapes(t, n, k):
 
 
 # ---------------------------------------------------------------------------
-# M = 1
+# M = 1, on every kernel choice: "auto" (the library's own pick), "stream"
+# (register pipeline) and "rows" (row tiles wherever they apply)
 # ---------------------------------------------------------------------------
-def test_gemv_config0():
+KERNELS = ["auto", "stream", "rows"]
+
+
+@pytest.fixture
+def gemv_kernel(request):
+    B.pn_set_gemv_kernel(request.param)
+    yield request.param
+    B.pn_set_gemv_kernel("auto")
+
+
+def rows_waves():
+    return torch.cuda.get_device_properties(0).multi_processor_count * 4
+
+
+def rows_ok(t, k, offset=0):
+    nb = k // WPB[t]
+    return offset % 16 == 0 and nb % 8 == 0 and nb * 34 <= 1 << 24
+
+
+def m1_variant(kernel, t, k, offset=0, tiles=0):
+    """The kernel pn_gemv should report for this shape (the library's rules,
+    restated from include/pn.h); `tiles` = 16-row tiles of the launch."""
+    if kernel != "stream" and rows_ok(t, k, offset) and (kernel == "rows" or tiles >= 8 * rows_waves()):
+        return "gemv_rows"
+    nw = k // WPB[t] * 8
+    if nw % 64 == 0 and nw * (20 if t == "pn3t" else 16) <= 65536:
+        return "gemv_stream"
+    return "gemv_generic"
+
+
+def tiles_of(*ns):
+    return sum((n + 15) // 16 for n in ns)
+
+
+@pytest.mark.parametrize("gemv_kernel", KERNELS, indirect=True)
+def test_gemv_config0(gemv_kernel):
     c = synth.config0()
-    say("gemv config 0 pn3t 256x5120")
-    y = gpu_gemv(c["type"], c["W"], c["N"], c["K"], c["x"], expect_variant="gemv_stream")
+    say("gemv config 0 pn3t 256x5120 (%s)" % gemv_kernel)
+    y = gpu_gemv(c["type"], c["W"], c["N"], c["K"], c["x"], expect_variant=m1_variant(gemv_kernel, "pn3t", 5120, 0, tiles_of(256)))
     y64, a = pnref.gemv_f64(c["type"], c["W"], c["N"], c["K"], c["x"])
     assert_gemv_close(y, y64, a, "config 0")
 
 
-def test_gemv_config1():
+@pytest.mark.parametrize("gemv_kernel", KERNELS, indirect=True)
+def test_gemv_config1(gemv_kernel):
     c = synth.config1()
-    say("gemv config 1 pn4t 5120x17408")
-    y = gpu_gemv(c["type"], c["W"], c["N"], c["K"], c["x"], expect_variant="gemv_stream")
+    say("gemv config 1 pn4t 5120x17408 (%s)" % gemv_kernel)
+    y = gpu_gemv(c["type"], c["W"], c["N"], c["K"], c["x"], expect_variant=m1_variant(gemv_kernel, "pn4t", 17408, 0, tiles_of(5120)))
     y64, a = pnref.gemv_f64(c["type"], c["W"], c["N"], c["K"], c["x"])
     assert_gemv_close(y, y64, a, "config 1")
 
 
-def test_gemv2_config2():
+@pytest.mark.parametrize("gemv_kernel", KERNELS, indirect=True)
+def test_gemv2_config2(gemv_kernel):
     """Fused gate+up: weights N(0, 0.02) quantized by the oracle's quantizer."""
-    say("gemv2 config 2: quantize 2 x 17408x5120 on the CPU")
+    say("gemv2 config 2: quantize 2 x 17408x5120 on the CPU (%s)" % gemv_kernel)
     wg, wu, x = synth.config2_weights()
     qg = pnref.quantize("pn3t", wg, 17408, 5120)
     qu = pnref.quantize("pn3t", wu, 17408, 5120)
@@ -124,7 +162,7 @@ def test_gemv2_config2():
     y1 = torch.empty(17408, dtype=torch.float32, device="cuda")
     B.pn_gemv2("pn3t", W0, W1, 17408, 5120, xd, y0, y1)
     sync()
-    assert B.pn_variant_name(B.pn_last_variant()) == "gemv_stream"
+    assert B.pn_variant_name(B.pn_last_variant()) == m1_variant(gemv_kernel, "pn3t", 5120, 0, tiles_of(17408, 17408))
     for q, y, name in ((qg, y0, "gate"), (qu, y1, "up")):
         y64, a = pnref.gemv_f64("pn3t", q, 17408, 5120, x)
         assert_gemv_close(y.cpu().numpy(), y64, a, "config 2 " + name)
@@ -135,83 +173,145 @@ def test_gemv2_config2():
 
 
 EDGE_SHAPES = [
-    # (type, N, K, W byte offset, variant)
-    ("pn3t", 1, 640, 0, "gemv_stream"),        # one pass per row
-    ("pn3t", 13, 1280, 0, "gemv_stream"),      # N not a multiple of the tile
-    ("pn3t", 257, 5120, 2, "gemv_stream"),     # 2-aligned base
-    ("pn4t", 3, 512, 0, "gemv_stream"),
-    ("pn4t", 1023, 6144, 2, "gemv_stream"),
-    ("pn4t", 200000, 512, 0, "gemv_stream"),   # many rows per wave
-    ("pn4t", 64, 17408, 6, "gemv_stream"),
-    ("pn3t", 5, 80, 0, "gemv_generic"),        # one block per row
-    ("pn3t", 9, 240, 2, "gemv_generic"),       # ragged: 3 blocks
-    ("pn4t", 7, 576, 0, "gemv_generic"),       # ragged: 9 blocks
-    ("pn4t", 33, 64 * 600, 0, "gemv_generic"), # activation larger than LDS
-    ("pn3t", 4, 80 * 500, 2, "gemv_generic"),
+    # (type, N, K, W byte offset)
+    ("pn3t", 1, 640, 0),          # one pass per row
+    ("pn3t", 13, 1280, 0),        # N not a multiple of the tile
+    ("pn3t", 257, 5120, 2),       # 2-aligned base
+    ("pn4t", 3, 512, 0),
+    ("pn4t", 1023, 6144, 2),
+    ("pn4t", 200000, 512, 0),     # many rows per wave
+    ("pn4t", 64, 17408, 6),
+    ("pn3t", 5, 80, 0),           # one block per row
+    ("pn3t", 9, 240, 2),          # ragged: 3 blocks
+    ("pn4t", 7, 576, 0),          # ragged: 9 blocks
+    ("pn4t", 33, 64 * 600, 0),    # activation larger than LDS
+    ("pn3t", 4, 80 * 500, 2),
+    # shapes of the row-tile kernel: P = periods (8 blocks) per row, 4 per window
+    ("pn3t", 1, 5120, 0),         # one row: a tile of 1 valid row
+    ("pn3t", 17, 80 * 24, 0),     # P = 3: one window, three of four lane rows
+    ("pn4t", 33, 64 * 40, 0),     # P = 5: the second window has one period
+    ("pn4t", 16, 5120, 0),        # P = 10: one whole tile, last window half used
+    ("pn4t", 31, 64 * 8 * 7, 0),  # P = 7, a ragged second tile
+    ("pn3t", 2000, 80 * 128, 0),  # P = 16: four whole windows
+    ("pn3t", 100, 5120, 16),      # 16-aligned, not 256-aligned base
+    ("pn3t", 100, 5120, 4),       # 4-aligned base: not for row tiles
+    ("pn4t", 1000, 17408, 0),     # P = 34: nine windows
+    ("pn3t", 3, 80 * 800, 0),     # P = 100: x of 128 KB (register kernel: generic)
+    ("pn3t", 200000, 5120, 0),    # 435 MB: many tiles per wave
+    ("pn4t", 4099, 6144, 0),      # P = 12, 257 tiles
 ]
 
 
-@pytest.mark.parametrize("t,n,k,offset,variant", EDGE_SHAPES)
-def test_gemv_edge_shapes(t, n, k, offset, variant):
-    say("gemv edge %s N=%d K=%d offset=%d" % (t, n, k, offset))
+@pytest.mark.parametrize("gemv_kernel", KERNELS, indirect=True)
+@pytest.mark.parametrize("t,n,k,offset", EDGE_SHAPES)
+def test_gemv_edge_shapes(gemv_kernel, t, n, k, offset):
+    say("gemv edge %s N=%d K=%d offset=%d (%s)" % (t, n, k, offset, gemv_kernel))
     w, g = random_matrix(n * 7 + k, t, n, k, unused_bits=True)
     x = synth.activation(g, k)
-    y = gpu_gemv(t, w, n, k, x, offset, expect_variant=variant)
+    y = gpu_gemv(t, w, n, k, x, offset, expect_variant=m1_variant(gemv_kernel, t, k, offset, tiles_of(n)))
     y64, a = pnref.gemv_f64(t, w, n, k, x)
     assert_gemv_close(y, y64, a, "%s %dx%d" % (t, n, k))
 
 
+@pytest.mark.parametrize("gemv_kernel", KERNELS, indirect=True)
 @pytest.mark.parametrize("t", ["pn3t", "pn4t"])
-def test_gemv_one_hot_is_exact(t):
-    """x = e_k gives the decoded column exactly, on both kernels."""
-    for n, k in ((40, WPB[t] * 8), (6, WPB[t] * 3)):
+def test_gemv_one_hot_is_exact(gemv_kernel, t):
+    """x = e_k gives the decoded column exactly, on every kernel."""
+    wpb = WPB[t]
+    cases = [(40, wpb * 8, (0, 1, wpb * 4 + 1, wpb * 8 - 1)), (6, wpb * 3, (0, 1, wpb + 1, wpb * 3 - 1)),
+             (9, wpb * 66, tuple(range(0, 2 * wpb)) + (wpb * 33, wpb * 33 + 1, wpb * 66 - 1))]
+    for n, k, kks in cases:
         w, g = random_matrix(3 + n, t, n, k)
         dense = pnref.dequantize(t, w, n, k)
-        for kk in (0, 1, k // 2 + 1, k - 1):
-            say("gemv one-hot %s %dx%d k=%d" % (t, n, k, kk))
+        say("gemv one-hot %s %dx%d, %d columns (%s)" % (t, n, k, len(kks), gemv_kernel))
+        for kk in kks:
             x = np.zeros(k, np.float16)
             x[kk] = 1.0
-            assert_bits_equal(gpu_gemv(t, w, n, k, x), dense[:, kk] + 0.0, "one-hot")
+            got = gpu_gemv(t, w, n, k, x, expect_variant=m1_variant(gemv_kernel, t, k, 0, tiles_of(n)))
+            assert_bits_equal(got + 0.0, dense[:, kk] + 0.0, "one-hot k=%d" % kk)
 
 
 @pytest.mark.parametrize("t", ["pn3t", "pn4t"])
-def test_gemv_zero_codes(t):
+def test_rows_one_hot_every_column(t):
+    """Row tiles, every column of a four-period window (both blocks of each
+    block pair, each lane's broadcast activation pairs) and of a partial
+    window: x = e_k gives the decoded column exactly."""
+    wpb = WPB[t]
+    n, k = 21, wpb * 8 * 5  # two tiles (the second ragged), windows of 4 and 1 periods
+    w, g = random_matrix(17, t, n, k)
+    dense = pnref.dequantize(t, w, n, k)
+    B.pn_set_gemv_kernel("rows")
+    try:
+        say("rows one-hot %s %dx%d, all %d columns" % (t, n, k, k))
+        raw = dev(np.ascontiguousarray(w).reshape(-1))
+        y = torch.empty(n, dtype=torch.float32, device="cuda")
+        x = torch.zeros(k, dtype=torch.float16, device="cuda")
+        got = np.empty((k, n), np.float32)
+        for kk in range(k):
+            x.zero_()
+            x[kk] = 1.0
+            B.pn_gemv(t, raw, n, k, x, y)
+            got[kk] = y.cpu().numpy()
+        assert B.pn_variant_name(B.pn_last_variant()) == "gemv_rows"
+        assert_bits_equal(got.T + 0.0, dense + 0.0, "one-hot every column")
+    finally:
+        B.pn_set_gemv_kernel("auto")
+
+
+@pytest.mark.parametrize("gemv_kernel", KERNELS, indirect=True)
+@pytest.mark.parametrize("t", ["pn3t", "pn4t"])
+def test_gemv_zero_codes(gemv_kernel, t):
     """All codes at z: every output is +-0 whatever x is."""
     blk = load_blocks()["G2" if t == "pn3t" else "G6"][1]
-    k = WPB[t] * 16
-    w = np.tile(blk, 16 * 9).reshape(9, -1)
-    x = np.random.default_rng(4).standard_normal(k).astype(np.float16)
-    say("gemv zero codes %s" % t)
-    y = gpu_gemv(t, w, 9, k, x)
-    assert np.all(y == 0)
+    for nblk in (16, 64):
+        k = WPB[t] * nblk
+        w = np.tile(blk, nblk * 9).reshape(9, -1)
+        x = np.random.default_rng(4).standard_normal(k).astype(np.float16)
+        say("gemv zero codes %s K=%d (%s)" % (t, k, gemv_kernel))
+        y = gpu_gemv(t, w, 9, k, x, expect_variant=m1_variant(gemv_kernel, t, k, 0, 1))
+        assert np.all(y == 0)
 
 
+@pytest.mark.parametrize("gemv_kernel", KERNELS, indirect=True)
 @pytest.mark.parametrize("t", ["pn3t", "pn4t"])
-def test_gemv_outlier_activations(t):
+def test_gemv_outlier_activations(gemv_kernel, t):
     """fp16 activations up to +-65504 (no fp16 accumulation anywhere)."""
-    n, k = 64, WPB[t] * 16
-    w, g = random_matrix(77, t, n, k)
-    x = synth.activation(g, k)
-    x[::97] = np.float16(65504.0)
-    x[5::89] = np.float16(-65504.0)
-    say("gemv outliers %s" % t)
-    y = gpu_gemv(t, w, n, k, x)
-    y64, a = pnref.gemv_f64(t, w, n, k, x)
-    assert_gemv_close(y, y64, a, "outliers")
+    for nblk in (16, 64):
+        n, k = 64, WPB[t] * nblk
+        w, g = random_matrix(77, t, n, k)
+        x = synth.activation(g, k)
+        x[::97] = np.float16(65504.0)
+        x[5::89] = np.float16(-65504.0)
+        say("gemv outliers %s K=%d (%s)" % (t, k, gemv_kernel))
+        y = gpu_gemv(t, w, n, k, x, expect_variant=m1_variant(gemv_kernel, t, k, 0, tiles_of(n)))
+        y64, a = pnref.gemv_f64(t, w, n, k, x)
+        assert_gemv_close(y, y64, a, "outliers")
 
 
-def test_gemv_deterministic():
+@pytest.mark.parametrize("gemv_kernel", KERNELS, indirect=True)
+def test_gemv_deterministic(gemv_kernel):
     c = synth.config0()
-    say("gemv determinism")
+    say("gemv determinism (%s)" % gemv_kernel)
     ys = [gpu_gemv(c["type"], c["W"], c["N"], c["K"], c["x"]) for _ in range(5)]
     for y in ys[1:]:
         assert_bits_equal(y, ys[0], "repeat")
 
 
-def test_group_mixed():
+GROUP_SPECS = {
+    # mixed: includes a row of one 8-block pass, so "auto" keeps the register kernel
+    "mixed": [("pn3t", 100, 5120), ("pn4t", 37, 5120), ("pn4t", 300, 6144), ("pn3t", 1, 640),
+              ("pn4t", 65, 17408), ("pn3t", 2000, 1280)],
+    # every problem fits the row-tile kernel (periods per row 8, 10, 12, 1, 34, 3, 7)
+    "rows": [("pn3t", 100, 5120), ("pn4t", 37, 5120), ("pn4t", 300, 6144), ("pn3t", 1, 640),
+             ("pn4t", 65, 17408), ("pn3t", 2000, 80 * 24), ("pn4t", 3, 64 * 56)],
+}
+
+
+@pytest.mark.parametrize("gemv_kernel", KERNELS, indirect=True)
+@pytest.mark.parametrize("which", ["mixed", "rows"])
+def test_group(gemv_kernel, which):
     """One grouped launch over problems of both types and several shapes."""
-    specs = [("pn3t", 100, 5120), ("pn4t", 37, 5120), ("pn4t", 300, 6144), ("pn3t", 1, 640),
-             ("pn4t", 65, 17408), ("pn3t", 2000, 1280)]
+    specs = GROUP_SPECS[which]
     host, probs = [], []
     for i, (t, n, k) in enumerate(specs):
         w, g = random_matrix(500 + i, t, n, k)
@@ -220,11 +320,18 @@ def test_group_mixed():
         y = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
         host.append((t, w, n, k, x, y))
         probs.append((t, wd, n, k, xd, y))
-    say("group of %d problems" % len(specs))
+    say("group %s of %d problems (%s)" % (which, len(specs), gemv_kernel))
+    tiles = tiles_of(*[n for _, n, _ in specs])
+    rows = all(m1_variant(gemv_kernel, t, k, 0, tiles) == "gemv_rows" for t, _, k in specs)
+    if not rows and not all(m1_variant("stream", t, k) == "gemv_stream" for t, _, k in specs):
+        with pytest.raises(B.PNError) as e:  # the register kernel takes whole 8-block passes only
+            B.Group(probs)
+        assert e.value.status == -4
+        return
     grp = B.Group(probs)
     grp.run()
     sync()
-    assert B.pn_variant_name(B.pn_last_variant()) == "gemv_stream_group"
+    assert B.pn_variant_name(B.pn_last_variant()) == ("gemv_rows_group" if rows else "gemv_stream_group")
     for t, w, n, k, x, y in host:
         y64, a = pnref.gemv_f64(t, w, n, k, x)
         assert_gemv_close(y.cpu().numpy(), y64, a, "group %s %dx%d" % (t, n, k))
