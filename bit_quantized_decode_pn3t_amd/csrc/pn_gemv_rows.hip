@@ -27,9 +27,10 @@
 // Loads.  A stage is one window of the tile: 16 rows x 1088 bytes, brought
 // to LDS by 17 aligned 16-byte DMA instructions (buffer_load_dwordx4 ... lds)
 // that each cover 1024 contiguous bytes of the matrix.  Each wave has a ring
-// of two stages and keeps one stage in flight while it computes the other;
-// x for a stage comes from global memory (L2) into registers, five dwordx4
-// per lane, issued with the stage's DMA.
+// of two stages; a stage's slot is refilled as soon as the lanes have read
+// their periods into registers, so two windows are in flight while one is
+// computed.  x for a stage comes from global memory (L2) into registers,
+// five dwordx4 per lane.
 //
 // Grid.  One workgroup of four waves per CU (the rings take 136 KiB of LDS).
 // Waves work independently on contiguous ranges of tiles, balanced by
@@ -50,17 +51,46 @@ using namespace pn::host;
 
 namespace {
 
-constexpr int kRWaves = 4;                    // waves per workgroup, one per SIMD
+// Design choices, measured on the 64-layer sweep:
+//   PN_ROWS_PAD    rows of a stage 1104 bytes apart in LDS (conflict-free
+//                  period reads, 18 DMA instructions a stage) or 1088 (17,
+//                  four-way bank conflicts);
+//   PN_ROWS_SPLIT  refill the ring slot after the first block pair's
+//                  products (the period reads have landed by then) rather
+//                  than waiting for the reads before any products;
+//   PN_ROWS_ILP    independent accumulation chains per block (1 or 2);
+//   PN_ROWS_STAGES ring stages per wave: 2 (4 waves per CU, one per SIMD,
+//                  two windows in flight per wave) or 1 (8 waves per CU,
+//                  two per SIMD: one computes while the other waits).
+#ifndef PN_ROWS_PAD
+#define PN_ROWS_PAD 1
+#endif
+#ifndef PN_ROWS_SPLIT
+#define PN_ROWS_SPLIT 1
+#endif
+#ifndef PN_ROWS_ILP
+#define PN_ROWS_ILP 2
+#endif
+#ifndef PN_ROWS_STAGES
+#define PN_ROWS_STAGES 1
+#endif
+
+constexpr int kNS = PN_ROWS_STAGES;           // ring stages per wave
+constexpr int kRWaves = kNS == 2 ? 4 : 8;      // waves per workgroup (one workgroup per CU)
 constexpr int kRThreads = 64 * kRWaves;
 constexpr int kTileRows = 16;                 // rows per tile: the lanes of a DPP row
 constexpr int kPeriod = 272;                  // 8 blocks
 constexpr int kWindow = 4 * kPeriod;          // tile-row bytes per stage
-constexpr int kStage = kTileRows * kWindow;   // 17,408
-constexpr int kDma = kStage / 1024;           // 17 DMA instructions per stage
+constexpr int kRowLds = PN_ROWS_PAD ? kWindow + 16 : kWindow;  // LDS bytes per tile row
+constexpr int kRowSlots = kRowLds / 16;      // 16-byte DMA slots per tile row
+constexpr int kDma = (kTileRows * kRowSlots + 63) / 64;  // DMA instructions per stage
+constexpr int kStage = 1024 * kDma;          // LDS bytes per stage
 constexpr int kXLoads = 5;                    // x loads per lane per stage
-constexpr int kLater = kDma + kXLoads;        // VMEM instructions of one stage
-constexpr int kRing = kRWaves * 2 * kStage;   // 139,264 bytes of LDS
-constexpr int kMinTilesPerWave = 8;           // below this "auto" uses gemv_stream
+constexpr int kLater = (kNS - 1) * (kDma + kXLoads);  // VMEM instructions issued after a stage
+constexpr int kRing = kRWaves * kNS * kStage;  // 147,456 (139,264 unpadded) bytes of LDS
+constexpr int kMinTilesPerCu = 32;            // below this "auto" uses gemv_stream
+constexpr int kPools = 16;                    // tile pools of a group launch
+constexpr int kCounterStride = 1024;          // uint32s between pool counters (4 KiB)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -79,20 +109,15 @@ struct RProb {
     int32_t type;      // 0 = pn3t, 1 = pn4t
 };
 
-// A wave's share of a group launch: its first tile and how many.
-struct RStart {
-    int32_t prob;
-    int32_t tile;
-    int32_t ntiles;
-    int32_t nitems;  // windows of those tiles
-};
-
 struct RArgs {
     const PN_CONST RProb *table;   // group plan, or null for the inline problems
-    const PN_CONST RStart *start;  // per wave (with the table)
+    const PN_CONST uint32_t *lut;  // group plan: tile k of the launch = problem
+                                   // lut[k] >> 20, tile lut[k] & 0xfffff
+    uint32_t *counters;            // group plan: pool p's counter at
+                                   // [kCounterStride * p], waves done after them
     RProb p0, p1;                  // inline problems (pn_gemv, pn_gemv2)
     int32_t count;                 // problems
-    int32_t total_tiles;           // inline problems: tiles of both
+    int32_t total_tiles;           // tiles of the launch
 };
 
 template <int I, int N, typename F>
@@ -138,13 +163,9 @@ __device__ __forceinline__ void word_dot(float &bs, uint32_t w, const u32x4 (&xs
     });
 }
 
-// Sum over one period of a row: sum over its 8 blocks of d * sum (n - z) x.
-template <int TYPE>
-__device__ __forceinline__ float period_dot(const uint8_t *src, const u32x4 (&xs)[kXLoads])
+// The lane's period of the stage: 17 chunks from LDS.
+__device__ __forceinline__ void load_period(const uint8_t *src, uint32_t (&D)[68])
 {
-    constexpr int PB = TYPE == 0 ? 40 : 32;  // activation pairs per block
-    constexpr int PW = TYPE == 0 ? 5 : 4;    // per word
-    uint32_t D[68];
 #pragma unroll
     for (int t = 0; t < 17; ++t) {
         const u32x4 v = *(const u32x4 *)(src + 16 * t);
@@ -153,34 +174,62 @@ __device__ __forceinline__ float period_dot(const uint8_t *src, const u32x4 (&xs
         D[4 * t + 2] = v[2];
         D[4 * t + 3] = v[3];
     }
-    float it = 0.0f;
-    static_for<0, 4>([&](auto bpc) {
-        constexpr int bp = decltype(bpc)::value;
-        constexpr int o = 17 * bp;
-        float bs = 0.0f;
-        static_for<0, 8>([&](auto jc) {
-            constexpr int j = decltype(jc)::value;
-            word_dot<TYPE, PB * (2 * bp) + PW * j>(bs, __builtin_amdgcn_alignbit(D[o + j + 1], D[o + j], 16), xs);
-        });
-        dot_done(bs);
-        it = __builtin_fmaf(half_bits_to_float(D[o] & 0xffffu), bs, it);
-        bs = 0.0f;
-        static_for<0, 8>([&](auto jc) {
-            constexpr int j = decltype(jc)::value;
-            word_dot<TYPE, PB * (2 * bp + 1) + PW * j>(bs, D[o + 9 + j], xs);
-        });
-        dot_done(bs);
-        it = __builtin_fmaf(half_bits_to_float(D[o + 8] >> 16), bs, it);
-    });
-    return it;
 }
 
-// Where a wave's issue side is in its work: problem, tile, window, tiles
-// left, and the problem's fields.  The cursor is advanced without nested
-// branches and the problem is reloaded (scalar loads) at every step, so that
-// every field is defined on every path and stays in scalar registers.
+// Block pairs [BP0, BP1) of a period of a row: it += d * sum (n - z) x over
+// their blocks.
+template <int TYPE, int BP0, int BP1>
+__device__ __forceinline__ void period_dot(const uint32_t (&D)[68], const u32x4 (&xs)[kXLoads], float &it)
+{
+    constexpr int PB = TYPE == 0 ? 40 : 32;  // activation pairs per block
+    constexpr int PW = TYPE == 0 ? 5 : 4;    // per word
+    static_for<BP0, BP1>([&](auto bpc) {
+        constexpr int bp = decltype(bpc)::value;
+        constexpr int o = 17 * bp;
+        static_for<0, 2>([&](auto hc) {  // block 2 bp + h of the period
+            constexpr int h = decltype(hc)::value;
+            float bs[PN_ROWS_ILP];
+#pragma unroll
+            for (int c = 0; c < PN_ROWS_ILP; ++c) bs[c] = 0.0f;
+            static_for<0, 8>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                // first block: words straddle the dword grid; second: whole dwords
+                const uint32_t w = h == 0 ? __builtin_amdgcn_alignbit(D[o + j + 1], D[o + j], 16) : D[o + 9 + j];
+                word_dot<TYPE, PB * (2 * bp + h) + PW * j>(bs[j % PN_ROWS_ILP], w, xs);
+            });
+#pragma unroll
+            for (int c = 0; c < PN_ROWS_ILP; ++c) dot_done(bs[c]);
+            float b = bs[0];
+#pragma unroll
+            for (int c = 1; c < PN_ROWS_ILP; ++c) b += bs[c];
+            const uint32_t dh = h == 0 ? D[o] & 0xffffu : D[o + 8] >> 16;
+            it = __builtin_fmaf(half_bits_to_float(dh), b, it);
+        });
+    });
+}
+
+// Where a wave's issue side is in its work: problem, tile, window, state,
+// and the problem's fields.  The cursor is advanced without nested branches
+// where possible and the problem is reloaded (scalar loads) at every step,
+// so that every field is defined on every path and stays in scalar
+// registers.
+//
+// Inline launches (one or two problems) split the tiles statically: wave w
+// takes tiles [T w / n, T (w + 1) / n).  Group launches hand out tiles
+// dynamically: the XCDs of an MI355X stream at measurably different rates
+// (up to 15 % apart on the sweep), so a static split leaves the fast ones
+// idle at the end.  One counter for the whole device would serialize the
+// grabs (device-scope atomics on one address, tens of ns each), so the
+// launch's tiles are dealt round-robin into kPools pools, one per half XCD,
+// each with its own counter; a wave takes tiles from its home pool and,
+// once that is empty, from the others in turn.  The grab for a wave's next
+// tile is issued at the start of the step after it moved to a new tile, and
+// read when it moves again, at least one step later.
+enum { kLive = 0, kIdle = 1, kDone = 2 };
+
 struct Cursor {
-    int32_t pi, tile, win, left;
+    int32_t pi, tile, win, state;
+    int32_t pool, tried;  // group: pool of the outstanding grab, pools found empty
     const uint8_t *W, *x;
     float *y;
     int32_t N, S, P, nwin, tiles, type;
@@ -218,81 +267,140 @@ __device__ __forceinline__ void load_prob(Cursor &c, const RArgs &a)
     }
 }
 
-template <bool TABLE>
-__device__ __forceinline__ void advance(Cursor &c, const RArgs &a)
+// Lane 0 takes the next tile of pool `pool` (the counter's old value lands
+// in k; lane 0 reads it later).  Inline asm keeps the compiler's atomic
+// optimizer from broadcasting the result right away, which would wait for
+// every load in flight; the instruction returns in issue order with the
+// stage's loads, and the kernel reads k only after a wait that covers it
+// (see the step).  Not visible to the compiler's wait analysis, it makes
+// that analysis more cautious, never less.
+__device__ __forceinline__ void grab(uint32_t *counters, int pool, int lane, uint32_t &k)
+{
+    if (lane == 0)
+        asm volatile("global_atomic_add %0, %1, %2, off sc0"
+                     : "=v"(k)
+                     : "v"(counters + kCounterStride * pool), "v"(1u)
+                     : "memory");
+}
+
+// Wait until at most kLater VMEM instructions are outstanding (every stage
+// before the ones issued after the one to compute is complete), and only
+// then let k be read.
+__device__ __forceinline__ void wait_stage_and(uint32_t &k)
+{
+    // (the builtin, so that the compiler's own wait analysis knows of it)
+    __builtin_amdgcn_s_waitcnt((((kLater >> 4) & 3) << 14) | 0x0f70 | (kLater & 15));
+    asm volatile("" : "+v"(k) :: "memory");
+}
+
+// Group launches: take the result of the outstanding grab (readable: the
+// caller has waited).  Index k of pool p is tile p + kPools k of the launch.
+// A live tile resets the search; an empty pool moves it to the next pool.
+// Unless every pool was found empty, grab again.
+__device__ __forceinline__ void next_tile(Cursor &c, const RArgs &a, int lane, uint32_t &gv)
+{
+    const uint32_t t = (uint32_t)c.pool + (uint32_t)kPools * (uint32_t)uniform((int32_t)gv);
+    if (t < (uint32_t)a.total_tiles) {
+        const uint32_t e = a.lut[t];
+        c.pi = (int32_t)(e >> 20);
+        c.tile = (int32_t)(e & 0xfffffu);
+        c.win = 0;
+        c.state = kLive;
+        c.tried = 0;
+        load_prob<true>(c, a);
+    } else {
+        c.tried += 1;
+        c.state = c.tried >= kPools ? kDone : kIdle;
+        c.pool = c.pool + 1 < kPools ? c.pool + 1 : 0;
+    }
+    if (c.state != kDone) grab(a.counters, c.pool, lane, gv);
+}
+
+// Inline launches: next window, next tile, next problem.
+__device__ __forceinline__ void advance_inline(Cursor &c, const RArgs &a, int32_t &left)
 {
     const int32_t win1 = c.win + 1;
-    const int32_t wrap_w = win1 >= c.nwin ? 1 : 0;
-    c.win = wrap_w ? 0 : win1;
-    c.left -= wrap_w;
-    const int32_t tile1 = c.tile + wrap_w;
+    const int32_t wrap = win1 >= c.nwin ? 1 : 0;
+    c.win = wrap ? 0 : win1;
+    left -= wrap;
+    const int32_t tile1 = c.tile + wrap;
     const int32_t wrap_t = tile1 >= c.tiles ? 1 : 0;
     c.tile = wrap_t ? 0 : tile1;
     c.pi += wrap_t;
-    load_prob<TABLE>(c, a);
+    c.state = left > 0 ? kLive : kDone;
+    load_prob<false>(c, a);
 }
 
 // What the compute side needs of a stage, recorded when the stage is issued.
 struct Slot {
-    float *y;
-    int32_t live, type, P, win, last, row0, N;
+    float *y;       // the tile's first output row
+    int32_t live;   // the stage holds work
+    int32_t done;   // no stage after this one holds work
+    int32_t type;
+    int32_t pv;     // periods of the window in the row (lane rows g < pv count)
+    int32_t last;   // the tile's last window
+    int32_t nrows;  // rows of the tile that exist
 };
 
-// Per-lane DMA offsets of the 17 instructions for row stride S: slot
-// q = 64 i + lane holds chunk q % 68 of tile row q / 68.
+// Per-lane DMA offsets for row stride S: slot q = 64 i + lane holds chunk
+// q % kRowSlots of tile row q / kRowSlots; pad slots and slots past the
+// last row get an out-of-range offset (they read nothing).
 __device__ __forceinline__ void dma_offsets(uint32_t (&vo)[kDma], int32_t S, int lane)
 {
 #pragma unroll
     for (int i = 0; i < kDma; ++i) {
         const uint32_t q = 64u * i + (uint32_t)lane;
-        const uint32_t row = q / 68u;
-        vo[i] = row * (uint32_t)S + 16u * (q - 68u * row);
+        const uint32_t row = q / (uint32_t)kRowSlots;
+        const uint32_t ck = q - (uint32_t)kRowSlots * row;
+        vo[i] = row < (uint32_t)kTileRows && ck < 68u ? row * (uint32_t)S + 16u * ck : 0x80000000u;
     }
 }
 
-// Issue the cursor's stage: the window's DMA into the ring stage and the x
-// loads into xs.  A cursor past its last tile issues the same instructions
-// on empty buffer ranges (they read nothing and return zeros), so every
-// stage is exactly kLater VMEM instructions.
-__device__ __forceinline__ void issue(const Cursor &c, uint8_t *stage, const uint32_t (&vo)[kDma], uint32_t xlane,
-                                      u32x4 (&xs)[kXLoads], Slot &sl)
+// The cursor's window into a ring stage: kDma DMA instructions.  A cursor
+// without a tile issues them on an empty buffer range (they read nothing and
+// write zeros), and chunks past the end of a row in a partial last window
+// are given an out-of-range offset, so that nothing is read twice.  Every
+// stage is exactly kDma + kXLoads VMEM instructions (issue_x below).
+__device__ __forceinline__ void issue_dma(const Cursor &c, uint8_t *stage, const uint32_t (&vo)[kDma], int lane)
 {
-    const bool live = c.left > 0;
-    const int32_t rows_left = c.N - kTileRows * c.tile;
-    const uint32_t rows = !live ? 0u : rows_left < kTileRows ? (uint32_t)rows_left : (uint32_t)kTileRows;
     // (readfirstlane: the resource must be in scalar registers, and the
     // compiler cannot always tell that these values are wave-uniform)
+    const bool live = c.state == kLive;
+    const int32_t rows_left = c.N - kTileRows * c.tile;
+    const uint32_t rows = !live ? 0u : rows_left < kTileRows ? (uint32_t)rows_left : (uint32_t)kTileRows;
     const uint8_t *wbase = uniform_ptr(c.W + (size_t)(kTileRows * c.tile) * (size_t)c.S);
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase, (uint32_t)uniform((int32_t)(rows * (uint32_t)c.S)));
     const uint32_t soff = (uint32_t)(c.win * kWindow);
+    const int32_t pv = c.P - 4 * c.win;  // periods of this window in the row
+    const uint32_t nck = pv >= 4 ? 68u : 17u * (uint32_t)pv;  // valid chunks per row
 #pragma unroll
-    for (int i = 0; i < kDma; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void *)(stage + 1024 * i), 16, (int)vo[i], (int)soff, 0,
+    for (int i = 0; i < kDma; ++i) {
+        const uint32_t q = 64u * i + (uint32_t)lane;
+        const uint32_t ck = q - (uint32_t)kRowSlots * (q / (uint32_t)kRowSlots);
+        const uint32_t off = ck < nck ? vo[i] : 0x80000000u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void *)(stage + 1024 * i), 16, (int)off, (int)soff, 0,
                                                  2 /* nontemporal */);
+    }
+}
+
+// The cursor's x for its window (lane (g, r): pairs 4r..4r+3 of each 64 of
+// period 4w + g), and what the compute side needs to know of the stage.
+__device__ __forceinline__ void issue_x(const Cursor &c, uint32_t xlane, u32x4 (&xs)[kXLoads], Slot &sl)
+{
+    const bool live = c.state == kLive;
     const uint32_t px = c.type == 0 ? 1280u : 1024u;  // x bytes per period
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(uniform_ptr(c.x), (uint32_t)uniform((int32_t)(live ? (uint32_t)c.P * px : 0u)));
     const uint32_t xsoff = 4u * (uint32_t)c.win * px;
 #pragma unroll
     for (int i = 0; i < kXLoads; ++i)
         xs[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(xlane + 256u * i), (int)xsoff, 0));
-    sl.y = c.y;
+    sl.y = c.y + kTileRows * c.tile;
     sl.live = live ? 1 : 0;
+    sl.done = c.state == kDone ? 1 : 0;
     sl.type = c.type;
-    sl.P = c.P;
-    sl.win = c.win;
+    sl.pv = live ? c.P - 4 * c.win : 0;
     sl.last = live && c.win == c.nwin - 1 ? 1 : 0;
-    sl.row0 = kTileRows * c.tile;
-    sl.N = c.N;
-}
-
-// Wait until at most kLater VMEM instructions are outstanding: the stage
-// issued last may still be in flight, everything before it has landed.
-// Loads (DMA included) return in issue order; stores only add to the count.
-// The empty asm keeps LDS reads of the stage below the wait.
-__device__ __forceinline__ void wait_stage()
-{
-    __builtin_amdgcn_s_waitcnt((((kLater >> 4) & 3) << 14) | 0x0f70 | (kLater & 15));
-    asm volatile("" ::: "memory");
+    sl.nrows = c.N - kTileRows * c.tile;
 }
 
 __device__ __forceinline__ void wait_lds_reads()
@@ -309,80 +417,137 @@ __global__ __launch_bounds__(kRThreads) void gemv_rows(RArgs a)
     const int wave = uniform(threadIdx.x >> 6);
     const int gw = blockIdx.x * kRWaves + wave;
     const int g = lane >> 4, r = lane & 15;
-    uint8_t *ring = lds + wave * 2 * kStage;
+    uint8_t *ring = lds + wave * kNS * kStage;
 
-    // this wave's tiles and windows
     Cursor ci;
-    int32_t nitems;
+    ci.win = 0;
+    ci.tried = 0;
+    int32_t left = 0;  // inline launches: tiles left
+    uint32_t gv = 0;   // lane 0: result of the outstanding grab
     if constexpr (TABLE) {
-        const PN_CONST RStart &st = a.start[gw];
-        ci.pi = st.prob;
-        ci.tile = st.tile;
-        ci.left = st.ntiles;
-        nitems = st.nitems;
+        // home pool: workgroups go to the XCDs in turn (blockIdx % 8), and a
+        // pool serves half of an XCD's CUs
+        ci.pool = (int)((blockIdx.x & 7) * 2 + ((blockIdx.x >> 3) & 1)) % kPools;
+        grab(a.counters, ci.pool, lane, gv);
+        asm volatile("s_waitcnt vmcnt(0)" : "+v"(gv) :: "memory");
+        next_tile(ci, a, lane, gv);
     } else {
         const int nw = gridDim.x * kRWaves;
         const int t0 = (int)((int64_t)a.total_tiles * gw / nw);
         const int t1 = (int)((int64_t)a.total_tiles * (gw + 1) / nw);
         ci.pi = t0 >= a.p0.tiles ? 1 : 0;
         ci.tile = t0 - (ci.pi ? a.p0.tiles : 0);
-        ci.left = t1 - t0;
-        nitems = ci.left * a.p0.nwin;
+        left = t1 - t0;
+        ci.state = left > 0 ? kLive : kDone;
+        load_prob<false>(ci, a);
     }
-    ci.win = 0;
-    if (nitems <= 0) return;
-    load_prob<TABLE>(ci, a);
-
-    uint32_t vo[kDma];
-    int32_t vo_s = ci.S;
-    dma_offsets(vo, vo_s, lane);
-    const uint32_t xl3 = (uint32_t)(16 * r + 1280 * g), xl4 = (uint32_t)(16 * r + 1024 * g);
-
-    u32x4 xs0[kXLoads], xs1[kXLoads];
-    Slot sl0, sl1;
-    issue(ci, ring, vo, ci.type == 0 ? xl3 : xl4, xs0, sl0);
-    advance<TABLE>(ci, a);
-    asm volatile("" ::: "memory");  // keep the two stages' loads in issue order
-    issue(ci, ring + kStage, vo, ci.type == 0 ? xl3 : xl4, xs1, sl1);
-    advance<TABLE>(ci, a);
-    float acc = 0.0f;
-
-    // One step: compute the stage in ring slot `stage`, then refill that slot
-    // with the issue cursor's stage.  A step past the wave's last window
-    // computes zeros and stores nothing.
-    auto step = [&](uint8_t *stage, u32x4 (&xs)[kXLoads], Slot &sl) {
-        wait_stage();
-        const uint8_t *src = stage + r * kWindow + g * kPeriod;
-        float it;
-        if (sl.type == 0)
-            it = period_dot<0>(src, xs);
-        else
-            it = period_dot<1>(src, xs);
-        acc += 4 * sl.win + g < sl.P ? it : 0.0f;
-        if (sl.last) {
-            // the tile is done: add the four DPP rows' sums of each row
-            auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc), __float_as_uint(acc), false, false);
-            float v = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
-            auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-            v = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
-            const int row = sl.row0 + r;
-            if (g == 0 && row < sl.N) sl.y[row] = v;
-            acc = 0.0f;
+    // Next window.  A group cursor leaving its tile, or without one, takes
+    // the grabbed tile (gv must be readable: the caller has waited).
+    auto advance = [&]() {
+        if constexpr (TABLE) {
+            if (ci.state == kIdle || (ci.state == kLive && ++ci.win >= ci.nwin)) next_tile(ci, a, lane, gv);
+        } else {
+            advance_inline(ci, a, left);
         }
-        wait_lds_reads();
-        if (ci.S != vo_s) {
-            vo_s = ci.S;
-            dma_offsets(vo, vo_s, lane);
-        }
-        issue(ci, stage, vo, ci.type == 0 ? xl3 : xl4, xs, sl);
-        advance<TABLE>(ci, a);
     };
-    for (int k = 0; k < nitems; k += 2) {
-        step(ring, xs0, sl0);
-        step(ring + kStage, xs1, sl1);
+
+    if (ci.state != kDone) {
+        uint32_t vo[kDma];
+        int32_t vo_s = ci.S;
+        dma_offsets(vo, vo_s, lane);
+        const uint32_t xl3 = (uint32_t)(16 * r + 1280 * g), xl4 = (uint32_t)(16 * r + 1024 * g);
+
+        u32x4 xs0[kXLoads], xs1[kXLoads];
+        Slot sl0, sl1;
+        issue_dma(ci, ring, vo, lane);
+        issue_x(ci, ci.type == 0 ? xl3 : xl4, xs0, sl0);
+        if constexpr (kNS == 2) {
+            // the second stage (each step starts by moving the cursor on)
+            if constexpr (TABLE) wait_stage_and(gv);  // the grab is older than stage 0
+            advance();
+            asm volatile("" ::: "memory");  // keep the two stages' loads in issue order
+            if (ci.S != vo_s) {
+                vo_s = ci.S;
+                dma_offsets(vo, vo_s, lane);
+            }
+            issue_dma(ci, ring + kStage, vo, lane);
+            issue_x(ci, ci.type == 0 ? xl3 : xl4, xs1, sl1);
+        }
+        float acc = 0.0f;
+
+        // One step.  The stage in ring slot `stage` has landed (and so has any
+        // grab issued before the later stages): move the issue cursor on, read
+        // the lane's period into registers, and as soon as the reads are done
+        // refill the slot with the issue cursor's window, so that windows are
+        // in flight while this one is computed.  With two stages per wave the
+        // cursor's x goes into xs once this stage's x is no longer needed;
+        // with one, into the other register set (xn, sn) right away.  A stage
+        // without work computes zeros and stores nothing.
+        auto step = [&](uint8_t *stage, u32x4 (&xs)[kXLoads], Slot &sl, u32x4 (&xn)[kXLoads], Slot &sn) {
+            wait_stage_and(gv);
+            advance();
+            // The cursor's scalar loads land before the period reads are
+            // issued: scalar loads return out of order and share lgkmcnt
+            // with LDS reads, so one still in flight would make the first
+            // use of D wait for all 17 reads.
+            wait_lds_reads();
+            uint32_t D[68];
+            load_period(stage + r * kRowLds + g * kPeriod, D);
+            float it = 0.0f;
+            if (PN_ROWS_SPLIT) {
+                // the first block pair's products while the other reads land
+                if (sl.type == 0)
+                    period_dot<0, 0, 1>(D, xs, it);
+                else
+                    period_dot<1, 0, 1>(D, xs, it);
+            }
+            wait_lds_reads();
+            if (ci.S != vo_s) {
+                vo_s = ci.S;
+                dma_offsets(vo, vo_s, lane);
+            }
+            issue_dma(ci, stage, vo, lane);
+            if constexpr (kNS == 1) issue_x(ci, ci.type == 0 ? xl3 : xl4, xn, sn);
+            if (sl.type == 0)
+                period_dot<0, PN_ROWS_SPLIT, 4>(D, xs, it);
+            else
+                period_dot<1, PN_ROWS_SPLIT, 4>(D, xs, it);
+            acc += g < sl.pv ? it : 0.0f;
+            if (sl.last) {
+                // the tile is done: add the four DPP rows' sums of each row
+                auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc), __float_as_uint(acc), false, false);
+                float v = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+                auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+                v = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+                if (g == 0 && r < sl.nrows) sl.y[r] = v;
+                acc = 0.0f;
+            }
+            if constexpr (kNS == 2) {
+                asm volatile("" ::: "memory");  // this stage's x loads after its DMA, in issue order
+                issue_x(ci, ci.type == 0 ? xl3 : xl4, xs, sl);
+            }
+        };
+        for (;;) {
+            if (sl0.done) break;
+            step(ring, xs0, sl0, xs1, sl1);
+            if (sl1.done) break;
+            step(ring + (kNS - 1) * kStage, xs1, sl1, xs0, sl0);
+        }
     }
-    // no DMA may still be writing this wave's LDS when the workgroup ends
-    __builtin_amdgcn_s_waitcnt(0x0f70);
+    // no DMA (or grab) may still be in flight when the wave ends
+    asm volatile("s_waitcnt vmcnt(0)" : "+v"(gv) :: "memory");
+    if constexpr (TABLE) {
+        // The last wave to finish resets the plan's counters for its next run.
+        if (lane == 0) {
+            const uint32_t nw = gridDim.x * kRWaves;
+            uint32_t *done = a.counters + kCounterStride * kPools;
+            if (__hip_atomic_fetch_add(done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == nw - 1) {
+                for (int p = 0; p < kPools; ++p)
+                    __hip_atomic_store(a.counters + kCounterStride * p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -450,7 +615,7 @@ bool pn::host::rows_ok(int t, const void *W, int64_t K, const void *x)
 bool pn::host::rows_pays(int64_t tiles)
 {
     if (pn_get_gemv_kernel() == PN_GEMV_ROWS) return true;
-    return tiles >= (int64_t)kMinTilesPerWave * rows_waves();
+    return tiles >= (int64_t)kMinTilesPerCu * device_cus();
 }
 
 int64_t pn::host::rows_tiles(int64_t N) { return (N + kTileRows - 1) / kTileRows; }
@@ -474,58 +639,55 @@ pn_status pn::host::rows_launch(int t, const void *W0, const void *W1, int64_t N
 pn_status pn::host::rows_group_create(const pn_gemv_desc *descs, int count, pn_group **out)
 {
     *out = nullptr;
-    const int nw = rows_waves();
-    const size_t tbytes = sizeof(RProb) * (size_t)count;
-    const size_t sbytes = sizeof(RStart) * (size_t)nw;
-    uint8_t *blob = (uint8_t *)calloc(1, tbytes + sbytes);
-    pn_group *g = (pn_group *)calloc(1, sizeof(pn_group));
-    if (!g || !blob) {
-        free(blob);
-        free(g);
-        return PN_ENOMEM;
-    }
-    RProb *host = (RProb *)blob;
-    int64_t windows = 0;  // the launch's stages: the unit of balance
+    if (count > 4096) return PN_EUNSUPPORTED;  // the tile table packs 12 bits of problem
+    RProb *host = (RProb *)calloc((size_t)count, sizeof(RProb));
+    if (!host) return PN_ENOMEM;
+    int64_t total = 0;
+    int maxwin = 0;
     for (int i = 0; i < count; ++i) {
         const pn_gemv_desc &e = descs[i];
         rfill(host[i], e.type, e.W, e.N, e.K, e.x, e.y);
-        windows += (int64_t)host[i].tiles * host[i].nwin;
-    }
-    // Wave w takes the tiles whose first window falls in its equal share
-    // [windows * w / nw, windows * (w + 1) / nw) of the launch's windows.
-    RStart *st = (RStart *)(blob + tbytes);
-    int pi = 0, tile = 0;
-    int64_t pos = 0;  // first window of (pi, tile)
-    for (int w = 0; w < nw; ++w) {
-        const int64_t lo = windows * w / nw, hi = windows * (w + 1) / nw;
-        while (pi < count && pos < lo) {  // skip tiles that start before the share
-            pos += host[pi].nwin;
-            if (++tile == host[pi].tiles) {
-                tile = 0;
-                ++pi;
-            }
+        if (host[i].tiles > (1 << 20)) {  // and 20 bits of tile
+            free(host);
+            return PN_EUNSUPPORTED;
         }
-        st[w].prob = pi;
-        st[w].tile = tile;
-        int n = 0, items = 0;
-        while (pi < count && pos < hi) {
-            pos += host[pi].nwin;
-            items += host[pi].nwin;
-            ++n;
-            if (++tile == host[pi].tiles) {
-                tile = 0;
-                ++pi;
-            }
-        }
-        st[w].ntiles = n;
-        st[w].nitems = items;
+        total += host[i].tiles;
+        if (host[i].nwin > maxwin) maxwin = host[i].nwin;
     }
-    if (hipMalloc(&g->table, tbytes + sbytes) != hipSuccess) {
+    if (total >= INT32_MAX) {
+        free(host);
+        return PN_EUNSUPPORTED;
+    }
+    // The plan: problems, the launch's tiles in the order they are handed out
+    // (longest first, so that the last tiles of a run are short ones; pool p
+    // takes every kPools-th of them from p), and the pools' counters and the
+    // count of finished waves, 4 KiB apart.
+    const size_t tbytes = sizeof(RProb) * (size_t)count;
+    const size_t lbytes = sizeof(uint32_t) * (size_t)total;
+    const size_t cbytes = sizeof(uint32_t) * kCounterStride * (kPools + 1);
+    const size_t loff = tbytes, coff = (tbytes + lbytes + 4095) & ~(size_t)4095;
+    uint8_t *blob = (uint8_t *)calloc(1, coff + cbytes);
+    pn_group *g = (pn_group *)calloc(1, sizeof(pn_group));
+    if (!g || !blob) {
+        free(host);
         free(blob);
         free(g);
         return PN_ENOMEM;
     }
-    if (hipMemcpy(g->table, blob, tbytes + sbytes, hipMemcpyHostToDevice) != hipSuccess) {
+    memcpy(blob, host, tbytes);
+    uint32_t *lut = (uint32_t *)(blob + loff);
+    size_t k = 0;
+    for (int w = maxwin; w >= 1; --w)
+        for (int i = 0; i < count; ++i)
+            if (host[i].nwin == w)
+                for (int t = 0; t < host[i].tiles; ++t) lut[k++] = ((uint32_t)i << 20) | (uint32_t)t;
+    free(host);
+    if (hipMalloc(&g->table, coff + cbytes) != hipSuccess) {
+        free(blob);
+        free(g);
+        return PN_ENOMEM;
+    }
+    if (hipMemcpy(g->table, blob, coff + cbytes, hipMemcpyHostToDevice) != hipSuccess) {
         (void)hipFree(g->table);
         free(blob);
         free(g);
@@ -534,21 +696,22 @@ pn_status pn::host::rows_group_create(const pn_gemv_desc *descs, int count, pn_g
     free(blob);
     g->kind = kGroupGemvRows;
     g->count = count;
-    g->total_tiles = nw;
+    g->total_tiles = (int)total;
     g->lds = kRing;
-    g->flags = 0;
+    g->flags = (int)coff;  // byte offset of the counters
     *out = g;
     return PN_OK;
 }
 
 pn_status pn::host::rows_group_run(const pn_group *g, hipStream_t s)
 {
-    if (g->total_tiles != rows_waves()) return PN_EUNSUPPORTED;  // made for another device
     RArgs a;
     memset(&a, 0, sizeof(a));
     a.table = (const PN_CONST RProb *)g->table;
-    a.start = (const PN_CONST RStart *)((const uint8_t *)g->table + sizeof(RProb) * (size_t)g->count);
+    a.lut = (const PN_CONST uint32_t *)((const uint8_t *)g->table + sizeof(RProb) * (size_t)g->count);
+    a.counters = (uint32_t *)((uint8_t *)g->table + g->flags);
     a.count = g->count;
+    a.total_tiles = g->total_tiles;
     return rlaunch(a, s, kVarGroupRows);
 }
 

@@ -114,9 +114,9 @@ pn_smallm_math pn_get_smallm_math(void);
  *                   default.  The row-tile kernel applies to rows of whole
  *                   8-block periods (K a multiple of 640 for pn3t, 512 for
  *                   pn4t) with 16-byte-aligned W and x; "large enough" is at
- *                   least 8 sixteen-row tiles per wave of the device (8192
- *                   tiles, 131,072 rows, on a 256-CU MI355X), because it
- *                   balances its work in whole tiles;
+ *                   least 32 sixteen-row tiles per compute unit (8192 tiles,
+ *                   131,072 rows, on a 256-CU MI355X), because one or two
+ *                   problems are split among its waves in whole tiles;
  *   PN_GEMV_STREAM  always the register-pipeline kernel;
  *   PN_GEMV_ROWS    the row-tile kernel wherever it applies, whatever the
  *                   launch size.
@@ -188,9 +188,9 @@ void pn_group_destroy(pn_group *g);
  * measured in the same harness as the GEMV (the v100-skinny README, "Kernel
  * benchmarks", rates its kernels against a measured read-only ceiling).  One
  * launch reads `*bytes_read` bytes (the largest multiple of the launch's
- * granule not above `bytes`, at least 1 KiB per wave) from `buf` with
- * coalesced 16-byte nontemporal loads and writes a checksum word per lane to
- * `scratch`.
+ * granule not above `bytes`, at least 16 KiB per wave) from `buf` with
+ * 16-byte nontemporal DMA loads into LDS (each wave a contiguous share) and
+ * writes a checksum word per lane to `scratch`.
  *   buf     : device, 16-byte aligned, `bytes` readable
  *   scratch : device, 4-byte aligned, pn_read_probe_scratch_bytes() bytes
  * Returns PN_ESHAPE if `bytes` is too small or `scratch_bytes` too small. */

@@ -107,8 +107,8 @@ def gemv_kernel(request):
     B.pn_set_gemv_kernel("auto")
 
 
-def rows_waves():
-    return torch.cuda.get_device_properties(0).multi_processor_count * 4
+def rows_min_tiles():
+    return torch.cuda.get_device_properties(0).multi_processor_count * 32
 
 
 def rows_ok(t, k, offset=0):
@@ -119,7 +119,7 @@ def rows_ok(t, k, offset=0):
 def m1_variant(kernel, t, k, offset=0, tiles=0):
     """The kernel pn_gemv should report for this shape (the library's rules,
     restated from include/pn.h); `tiles` = 16-row tiles of the launch."""
-    if kernel != "stream" and rows_ok(t, k, offset) and (kernel == "rows" or tiles >= 8 * rows_waves()):
+    if kernel != "stream" and rows_ok(t, k, offset) and (kernel == "rows" or tiles >= rows_min_tiles()):
         return "gemv_rows"
     nw = k // WPB[t] * 8
     if nw % 64 == 0 and nw * (20 if t == "pn3t" else 16) <= 65536:

@@ -43,7 +43,9 @@ def _wait_states(line):
 
 
 def find_hazards(asm):
-    """Return descriptions of DPP-read and dot-write hazards in `asm`."""
+    """Return descriptions of DPP-read and dot-write hazards in `asm`, and of
+    any use of a hand-issued atomic's result register before a vmcnt wait
+    (the compiler does not know the register is still being written)."""
     lines = [l.split(";")[0].strip() for l in asm.splitlines()]
     ins = [l for l in lines if l and not l.startswith((".", "//")) and not l.endswith(":")]
     found = []
@@ -66,6 +68,25 @@ def find_hazards(asm):
                     found.append("dot write -> use after %d wait states: %s -> %s" % (ws, line, nxt))
                     break
                 ws += _wait_states(nxt)
+        if op.startswith("global_atomic") and args and " sc0" in line:
+            dst = _regs(args[0])
+            for nxt in ins[i + 1:]:
+                op2, a2 = _split(nxt)
+                if op2.startswith(("s_cbranch", "s_branch", "s_setpc", "s_endpgm")) or \
+                        (op2 == "s_waitcnt" and "vmcnt" in nxt):
+                    break
+                touched = set()
+                for j, t in enumerate(a2):
+                    rs = _regs(t.split()[0]) if t else set()
+                    # the compiler does 32-bit multiply-adds with
+                    # v_mad_u64_u32 and leaves the addend's high half
+                    # undefined: a read of it there is not a use
+                    if j == 4 and op2.startswith("v_mad_u64_u32") and len(rs) == 2 and dst & rs == {max(rs)}:
+                        continue
+                    touched |= rs
+                if dst & touched:
+                    found.append("atomic result used before a wait: %s -> %s" % (line, nxt))
+                    break
         if "_dpp" in op and len(args) > 1:
             src0 = _regs(args[1])
             for back in (1, 2):
@@ -89,11 +110,15 @@ def test_checker_flags_a_planted_hazard():
     v_dot2c_f32_f16_dpp v12, v1, v3 row_newbcast:4 row_mask:0xf bank_mask:0xf
     s_nop 2
     v_fma_mix_f32 v20, v4, v12, v20
+    global_atomic_add v30, v[2:3], v31, off sc0
+    v_mov_b32_e32 v32, v30
+    s_waitcnt vmcnt(0)
     """
     got = find_hazards(planted)
-    assert len(got) == 2, got
+    assert len(got) == 3, got
     assert "v_fma_mix_f32 v20, v4, v10" in got[0]
     assert "v_mov_b32_e32 v7" in got[1]
+    assert "v_mov_b32_e32 v32, v30" in got[2]
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None, reason="no hipcc")
