@@ -7,7 +7,8 @@ it, and (b) three wait states between a dot instruction's write of its
 accumulator and any other instruction that reads or writes that register
 (a chain of the same dot instruction accumulating into it is forwarded).
 A missing (b) drops the last product of a block: exactly the failure this
-test guards against.  The kernel is compiled to gfx950 assembly here (no GPU
+test guards against.  Wait states are counted as the hardware does (an
+s_nop n is n + 1 of them).  The kernel is compiled to gfx950 assembly here (no GPU
 needed) and every such instruction is checked in straight-line code."""
 import os
 import re
@@ -89,14 +90,17 @@ def find_hazards(asm):
                     break
         if "_dpp" in op and len(args) > 1:
             src0 = _regs(args[1])
-            for back in (1, 2):
-                if i - back < 0:
+            ws = 0
+            for back in range(1, 4):
+                if i - back < 0 or ws >= 2:
                     break
                 prev = ins[i - back]
                 pop, pa = _split(prev)
                 if pop.startswith("v_") and pa and not pop.startswith(("v_readfirstlane", "v_readlane", "v_cmp")) \
                         and (_regs(pa[0]) & src0):
-                    found.append("VALU write -> DPP read: %s -> %s" % (prev, line))
+                    found.append("VALU write -> DPP read after %d wait states: %s -> %s" % (ws, prev, line))
+                    break
+                ws += _wait_states(prev)
     return found
 
 
@@ -113,12 +117,19 @@ def test_checker_flags_a_planted_hazard():
     global_atomic_add v30, v[2:3], v31, off sc0
     v_mov_b32_e32 v32, v30
     s_waitcnt vmcnt(0)
+    v_add_f32_e32 v40, v41, v42
+    s_nop 1
+    v_add_f32_dpp v43, v40, v43 row_shr:1 row_mask:0xf bank_mask:0xf
+    v_add_f32_e32 v44, v41, v42
+    s_nop 0
+    v_add_f32_dpp v45, v44, v45 row_shr:1 row_mask:0xf bank_mask:0xf
     """
     got = find_hazards(planted)
-    assert len(got) == 3, got
+    assert len(got) == 4, got
     assert "v_fma_mix_f32 v20, v4, v10" in got[0]
     assert "v_mov_b32_e32 v7" in got[1]
     assert "v_mov_b32_e32 v32, v30" in got[2]
+    assert "v_add_f32_e32 v44" in got[3]  # s_nop 0 is one wait state; s_nop 1 before v43's read is enough
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None, reason="no hipcc")
