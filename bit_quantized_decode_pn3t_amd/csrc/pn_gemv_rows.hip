@@ -25,17 +25,20 @@
 // There is no per-row wave reduction and no activation traffic through LDS.
 //
 // Loads.  A stage is one window of the tile: 16 rows x 1088 bytes, brought
-// to LDS by 17 aligned 16-byte DMA instructions (buffer_load_dwordx4 ... lds)
-// that each cover 1024 contiguous bytes of the matrix.  Each wave has a ring
-// of two stages; a stage's slot is refilled as soon as the lanes have read
-// their periods into registers, so two windows are in flight while one is
-// computed.  x for a stage comes from global memory (L2) into registers,
-// five dwordx4 per lane.
+// to LDS by 16-byte DMA instructions (buffer_load_dwordx4 ... lds), rows
+// 1104 bytes apart in LDS so that the lanes' period reads do not collide in
+// banks.  Each wave has one stage: once its lanes have read their periods
+// into registers, the stage is refilled with the wave's next window, in two
+// pieces between the block pairs' products, so that the next window is in
+// flight while this one is computed.  x for a stage comes from global
+// memory (L2) into registers, five dwordx4 per lane.
 //
-// Grid.  One workgroup of four waves per CU (the rings take 136 KiB of LDS).
-// Waves work independently on contiguous ranges of tiles, balanced by
-// windows; a launch with few tiles per wave balances badly, and the host
-// gives such launches to gemv_stream.
+// Grid.  One workgroup of eight waves per CU (two per SIMD: one computes
+// while the other waits; the stages take 144 KiB of LDS).  Inline launches
+// (one matrix, or the fused pair) split their tiles evenly over the waves;
+// group launches (many matrices, one launch) hand tiles out from pools of
+// per-pool atomic counters, longest tiles first.  A launch with few tiles
+// per wave balances badly, and the host gives such launches to gemv_stream.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -61,7 +64,10 @@ namespace {
 //   PN_ROWS_ILP    independent accumulation chains per block (1 or 2);
 //   PN_ROWS_STAGES ring stages per wave: 2 (4 waves per CU, one per SIMD,
 //                  two windows in flight per wave) or 1 (8 waves per CU,
-//                  two per SIMD: one computes while the other waits).
+//                  two per SIMD: one computes while the other waits);
+//   PN_ROWS_SPREAD pieces a stage's DMA is issued in, between the block
+//                  pairs' products (1: all at once, which stalls the wave
+//                  while the eight waves' bursts queue up; 2 or 3).
 #ifndef PN_ROWS_PAD
 #define PN_ROWS_PAD 1
 #endif
@@ -73,6 +79,9 @@ namespace {
 #endif
 #ifndef PN_ROWS_STAGES
 #define PN_ROWS_STAGES 1
+#endif
+#ifndef PN_ROWS_SPREAD
+#define PN_ROWS_SPREAD 2
 #endif
 
 constexpr int kNS = PN_ROWS_STAGES;           // ring stages per wave
@@ -91,6 +100,7 @@ constexpr int kRing = kRWaves * kNS * kStage;  // 147,456 (139,264 unpadded) byt
 constexpr int kMinTilesPerCu = 32;            // below this "auto" uses gemv_stream
 constexpr int kPools = 16;                    // tile pools of a group launch
 constexpr int kCounterStride = 1024;          // uint32s between pool counters (4 KiB)
+static_assert(kPools <= 32 && (kPools & (kPools - 1)) == 0, "pools: a power of two, one lane each");
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -222,14 +232,17 @@ __device__ __forceinline__ void period_dot(const uint32_t (&D)[68], const u32x4 
 // grabs (device-scope atomics on one address, tens of ns each), so the
 // launch's tiles are dealt round-robin into kPools pools, one per half XCD,
 // each with its own counter; a wave takes tiles from its home pool and,
-// once that is empty, from the others in turn.  The grab for a wave's next
-// tile is issued at the start of the step after it moved to a new tile, and
-// read when it moves again, at least one step later.
-enum { kLive = 0, kIdle = 1, kDone = 2 };
+// once that is empty, reads all the counters at once (one atomic add of
+// zero per lane) and moves to a pool with tiles left, or ends when none has
+// any.  (Trying the pools one by one cost a step per empty pool at the end
+// of every launch.)  The grab for a wave's next tile is issued at the start
+// of the step after it moved to a new tile, and read when it moves again,
+// at least one step later; so is the counter read.
+enum { kLive = 0, kIdle = 1, kDone = 2, kScan = 3 };
 
 struct Cursor {
     int32_t pi, tile, win, state;
-    int32_t pool, tried;  // group: pool of the outstanding grab, pools found empty
+    int32_t pool, rot;  // group: pool of the outstanding grab, where the wave starts looking
     const uint8_t *W, *x;
     float *y;
     int32_t N, S, P, nwin, tiles, type;
@@ -267,19 +280,24 @@ __device__ __forceinline__ void load_prob(Cursor &c, const RArgs &a)
     }
 }
 
-// Lane 0 takes the next tile of pool `pool` (the counter's old value lands
-// in k; lane 0 reads it later).  Inline asm keeps the compiler's atomic
-// optimizer from broadcasting the result right away, which would wait for
-// every load in flight; the instruction returns in issue order with the
-// stage's loads, and the kernel reads k only after a wait that covers it
-// (see the step).  Not visible to the compiler's wait analysis, it makes
+// The pool counters.  Lanes with `on` add `v` to pool p's counter and get
+// its old value in k; lane 0 adding 1 to its pool's counter takes that
+// pool's next tile (a grab), lanes 0 .. kPools - 1 adding 0 to every counter
+// read them all (a scan).  Inline asm keeps the compiler's atomic optimizer
+// from broadcasting the result right away, which would wait for every load
+// in flight; the instruction returns in issue order with the stage's loads,
+// and the kernel reads k only after a wait that covers it (see the step).
+// There is one such instruction in the loop and k is both its input and
+// output, so that the compiler has no reason to copy the result register
+// before that wait (a copy there reads it before the atomic has written
+// it).  Not visible to the compiler's wait analysis, the instruction makes
 // that analysis more cautious, never less.
-__device__ __forceinline__ void grab(uint32_t *counters, int pool, int lane, uint32_t &k)
+__device__ __forceinline__ void counter_op(uint32_t *counters, bool on, int p, uint32_t v, uint32_t &k)
 {
-    if (lane == 0)
+    if (on)
         asm volatile("global_atomic_add %0, %1, %2, off sc0"
-                     : "=v"(k)
-                     : "v"(counters + kCounterStride * pool), "v"(1u)
+                     : "+v"(k)
+                     : "v"(counters + kCounterStride * p), "v"(v)
                      : "memory");
 }
 
@@ -293,27 +311,39 @@ __device__ __forceinline__ void wait_stage_and(uint32_t &k)
     asm volatile("" : "+v"(k) :: "memory");
 }
 
-// Group launches: take the result of the outstanding grab (readable: the
-// caller has waited).  Index k of pool p is tile p + kPools k of the launch.
-// A live tile resets the search; an empty pool moves it to the next pool.
-// Unless every pool was found empty, grab again.
+// Group launches: take the result of the outstanding grab or counter read
+// (readable: the caller has waited).  Index k of pool p is tile p + kPools k
+// of the launch, so pool p has tiles left while p + kPools k < tiles.  A
+// grab that found its pool empty reads every counter; the read picks the
+// first pool with tiles left at or after the wave's own starting point (so
+// that the waves of an emptied pool spread over the others) and grabs from
+// it, or ends the wave.  Every grab and read moves the wave on: a pool's
+// counter only grows, so the wave ends after finitely many.
 __device__ __forceinline__ void next_tile(Cursor &c, const RArgs &a, int lane, uint32_t &gv)
 {
-    const uint32_t t = (uint32_t)c.pool + (uint32_t)kPools * (uint32_t)uniform((int32_t)gv);
-    if (t < (uint32_t)a.total_tiles) {
-        const uint32_t e = a.lut[t];
-        c.pi = (int32_t)(e >> 20);
-        c.tile = (int32_t)(e & 0xfffffu);
-        c.win = 0;
-        c.state = kLive;
-        c.tried = 0;
-        load_prob<true>(c, a);
+    if (c.state == kScan) {
+        const bool open = lane < kPools && (uint32_t)lane + (uint32_t)kPools * gv < (uint32_t)a.total_tiles;
+        const uint32_t m = (uint32_t)__builtin_amdgcn_ballot_w64(open) & ((1u << kPools) - 1u);
+        const uint32_t s = (uint32_t)c.rot;
+        const uint32_t rm = ((m >> s) | (m << (kPools - s))) & ((1u << kPools) - 1u);  // pool s at bit 0
+        c.pool = m != 0 ? (int32_t)(((uint32_t)__builtin_ctz(rm | (1u << kPools)) + s) & (uint32_t)(kPools - 1)) : c.pool;
+        c.state = m != 0 ? kIdle : kDone;
     } else {
-        c.tried += 1;
-        c.state = c.tried >= kPools ? kDone : kIdle;
-        c.pool = c.pool + 1 < kPools ? c.pool + 1 : 0;
+        const uint32_t t = (uint32_t)c.pool + (uint32_t)kPools * (uint32_t)uniform((int32_t)gv);
+        if (t < (uint32_t)a.total_tiles) {
+            const uint32_t e = a.lut[t];
+            c.pi = (int32_t)(e >> 20);
+            c.tile = (int32_t)(e & 0xfffffu);
+            c.win = 0;
+            c.state = kLive;
+            load_prob<true>(c, a);
+        } else {
+            c.state = kScan;
+        }
     }
-    if (c.state != kDone) grab(a.counters, c.pool, lane, gv);
+    const bool scan = c.state == kScan;
+    counter_op(a.counters, scan ? lane < kPools : c.state != kDone && lane == 0, scan ? lane : c.pool,
+               scan ? 0u : 1u, gv);
 }
 
 // Inline launches: next window, next tile, next problem.
@@ -360,8 +390,15 @@ __device__ __forceinline__ void dma_offsets(uint32_t (&vo)[kDma], int32_t S, int
 // without a tile issues them on an empty buffer range (they read nothing and
 // write zeros), and chunks past the end of a row in a partial last window
 // are given an out-of-range offset, so that nothing is read twice.  Every
-// stage is exactly kDma + kXLoads VMEM instructions (issue_x below).
-__device__ __forceinline__ void issue_dma(const Cursor &c, uint8_t *stage, const uint32_t (&vo)[kDma], int lane)
+// stage is exactly kDma + kXLoads VMEM instructions (issue_x below).  The
+// instructions are issued in pieces (dma_part), set up once (dma_setup).
+struct Dma {
+    __amdgpu_buffer_rsrc_t wr;
+    uint32_t soff;  // the window's byte offset in the tile's rows
+    uint32_t nck;   // valid chunks per row
+};
+
+__device__ __forceinline__ Dma dma_setup(const Cursor &c)
 {
     // (readfirstlane: the resource must be in scalar registers, and the
     // compiler cannot always tell that these values are wave-uniform)
@@ -369,18 +406,30 @@ __device__ __forceinline__ void issue_dma(const Cursor &c, uint8_t *stage, const
     const int32_t rows_left = c.N - kTileRows * c.tile;
     const uint32_t rows = !live ? 0u : rows_left < kTileRows ? (uint32_t)rows_left : (uint32_t)kTileRows;
     const uint8_t *wbase = uniform_ptr(c.W + (size_t)(kTileRows * c.tile) * (size_t)c.S);
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase, (uint32_t)uniform((int32_t)(rows * (uint32_t)c.S)));
-    const uint32_t soff = (uint32_t)(c.win * kWindow);
+    Dma d;
+    d.wr = make_rsrc(wbase, (uint32_t)uniform((int32_t)(rows * (uint32_t)c.S)));
+    d.soff = (uint32_t)(c.win * kWindow);
     const int32_t pv = c.P - 4 * c.win;  // periods of this window in the row
-    const uint32_t nck = pv >= 4 ? 68u : 17u * (uint32_t)pv;  // valid chunks per row
+    d.nck = pv >= 4 ? 68u : 17u * (uint32_t)pv;
+    return d;
+}
+
+template <int I0, int I1>
+__device__ __forceinline__ void dma_part(const Dma &d, uint8_t *stage, const uint32_t (&vo)[kDma], int lane)
+{
 #pragma unroll
-    for (int i = 0; i < kDma; ++i) {
+    for (int i = I0; i < I1; ++i) {
         const uint32_t q = 64u * i + (uint32_t)lane;
         const uint32_t ck = q - (uint32_t)kRowSlots * (q / (uint32_t)kRowSlots);
-        const uint32_t off = ck < nck ? vo[i] : 0x80000000u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void *)(stage + 1024 * i), 16, (int)off, (int)soff, 0,
+        const uint32_t off = ck < d.nck ? vo[i] : 0x80000000u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.wr, (lds_void *)(stage + 1024 * i), 16, (int)off, (int)d.soff, 0,
                                                  2 /* nontemporal */);
     }
+}
+
+__device__ __forceinline__ void issue_dma(const Cursor &c, uint8_t *stage, const uint32_t (&vo)[kDma], int lane)
+{
+    dma_part<0, kDma>(dma_setup(c), stage, vo, lane);
 }
 
 // The cursor's x for its window (lane (g, r): pairs 4r..4r+3 of each 64 of
@@ -421,14 +470,15 @@ __global__ __launch_bounds__(kRThreads) void gemv_rows(RArgs a)
 
     Cursor ci;
     ci.win = 0;
-    ci.tried = 0;
+    ci.state = kIdle;
+    ci.rot = gw & (kPools - 1);
     int32_t left = 0;  // inline launches: tiles left
     uint32_t gv = 0;   // lane 0: result of the outstanding grab
     if constexpr (TABLE) {
         // home pool: workgroups go to the XCDs in turn (blockIdx % 8), and a
         // pool serves half of an XCD's CUs
         ci.pool = (int)((blockIdx.x & 7) * 2 + ((blockIdx.x >> 3) & 1)) % kPools;
-        grab(a.counters, ci.pool, lane, gv);
+        counter_op(a.counters, lane == 0, ci.pool, 1u, gv);
         asm volatile("s_waitcnt vmcnt(0)" : "+v"(gv) :: "memory");
         next_tile(ci, a, lane, gv);
     } else {
@@ -445,7 +495,8 @@ __global__ __launch_bounds__(kRThreads) void gemv_rows(RArgs a)
     // the grabbed tile (gv must be readable: the caller has waited).
     auto advance = [&]() {
         if constexpr (TABLE) {
-            if (ci.state == kIdle || (ci.state == kLive && ++ci.win >= ci.nwin)) next_tile(ci, a, lane, gv);
+            if (ci.state == kIdle || ci.state == kScan || (ci.state == kLive && ++ci.win >= ci.nwin))
+                next_tile(ci, a, lane, gv);
         } else {
             advance_inline(ci, a, left);
         }
@@ -474,6 +525,13 @@ __global__ __launch_bounds__(kRThreads) void gemv_rows(RArgs a)
             issue_x(ci, ci.type == 0 ? xl3 : xl4, xs1, sl1);
         }
         float acc = 0.0f;
+        // A finished tile's sums are stored at the start of the next step,
+        // ahead of that step's loads, so that the wait for those loads does
+        // not also wait for the store to be acknowledged.
+        // (per lane, in VGPRs: scalar registers are all taken)
+        float pend_v = 0.0f;
+        float *pend_a = nullptr;  // this lane's output, if it stores one
+        int32_t pend = 0;
 
         // One step.  The stage in ring slot `stage` has landed (and so has any
         // grab issued before the later stages): move the issue cursor on, read
@@ -493,8 +551,10 @@ __global__ __launch_bounds__(kRThreads) void gemv_rows(RArgs a)
             wait_lds_reads();
             uint32_t D[68];
             load_period(stage + r * kRowLds + g * kPeriod, D);
+            if (pend) *pend_a = pend_v;
+            pend = 0;
             float it = 0.0f;
-            if (PN_ROWS_SPLIT) {
+            if (PN_ROWS_SPLIT && sl.live) {
                 // the first block pair's products while the other reads land
                 if (sl.type == 0)
                     period_dot<0, 0, 1>(D, xs, it);
@@ -506,12 +566,30 @@ __global__ __launch_bounds__(kRThreads) void gemv_rows(RArgs a)
                 vo_s = ci.S;
                 dma_offsets(vo, vo_s, lane);
             }
-            issue_dma(ci, stage, vo, lane);
+            // The refill, in PN_ROWS_SPREAD pieces between the remaining
+            // block pairs (sched_barrier keeps the compiler from gathering
+            // them again); a stage without work computes nothing.
+            const Dma dm = dma_setup(ci);
+            constexpr int kPiece = (kDma + PN_ROWS_SPREAD - 1) / PN_ROWS_SPREAD;
+            dma_part<0, kPiece>(dm, stage, vo, lane);
             if constexpr (kNS == 1) issue_x(ci, ci.type == 0 ? xl3 : xl4, xn, sn);
-            if (sl.type == 0)
-                period_dot<0, PN_ROWS_SPLIT, 4>(D, xs, it);
-            else
-                period_dot<1, PN_ROWS_SPLIT, 4>(D, xs, it);
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<PN_ROWS_SPLIT, 4>([&](auto bpc) {
+                constexpr int bp = decltype(bpc)::value;
+                if (sl.live) {
+                    if (sl.type == 0)
+                        period_dot<0, bp, bp + 1>(D, xs, it);
+                    else
+                        period_dot<1, bp, bp + 1>(D, xs, it);
+                }
+                constexpr int k = bp - PN_ROWS_SPLIT + 1;  // pieces issued after this block pair
+                if constexpr (k < PN_ROWS_SPREAD) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    dma_part<(k * kPiece < kDma ? k * kPiece : kDma), ((k + 1) * kPiece < kDma ? (k + 1) * kPiece : kDma)>(
+                        dm, stage, vo, lane);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            });
             acc += g < sl.pv ? it : 0.0f;
             if (sl.last) {
                 // the tile is done: add the four DPP rows' sums of each row
@@ -519,7 +597,9 @@ __global__ __launch_bounds__(kRThreads) void gemv_rows(RArgs a)
                 float v = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
                 auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
                 v = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
-                if (g == 0 && r < sl.nrows) sl.y[r] = v;
+                pend_v = v;
+                pend_a = sl.y + r;
+                pend = g == 0 && r < sl.nrows;
                 acc = 0.0f;
             }
             if constexpr (kNS == 2) {
@@ -533,6 +613,7 @@ __global__ __launch_bounds__(kRThreads) void gemv_rows(RArgs a)
             if (sl1.done) break;
             step(ring + (kNS - 1) * kStage, xs1, sl1, xs0, sl0);
         }
+        if (pend) *pend_a = pend_v;
     }
     // no DMA (or grab) may still be in flight when the wave ends
     asm volatile("s_waitcnt vmcnt(0)" : "+v"(gv) :: "memory");
