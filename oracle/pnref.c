@@ -268,3 +268,36 @@ int pnref_quantize(int type, const float *w, int64_t n, int64_t k, uint8_t *out)
     }
     return PNREF_OK;
 }
+
+/* Blockwise Hadamard rotation (see pnref.h).  Readings fixed here where the
+ * page is silent:
+ *   - block size B = 1024 in the library (the largest power of two that
+ *     divides every PN width of the model, 5120, 6144 and 17408); the oracle
+ *     takes any power of 4 so that small cases can be worked by hand;
+ *   - Sylvester order, H[i][j] = (-1)^popcount(i & j), and the orthonormal
+ *     scale 1/sqrt(B) (a power of two for B a power of 4, so exact);
+ *   - the result is rounded once to fp16 (the GEMV's activation type), ties
+ *     to even; an exact zero is +0.
+ * The sum runs sequentially in fp64 and is exact: every fp16 value is a
+ * multiple of 2^-24 below 2^16, so every partial sum of at most 1024 of them
+ * is a multiple of 2^-24 below 2^26, which binary64 holds exactly. */
+int pnref_rotate(const uint16_t *x, int64_t k, int64_t block, uint16_t *out)
+{
+    if (!x || !out || block < 1 || k < 0) return PNREF_EINVAL;
+    int lg = 0;
+    while (((int64_t)1 << lg) < block) ++lg;
+    if (((int64_t)1 << lg) != block || (lg & 1) || block > 1024) return PNREF_ESHAPE;
+    if (k % block != 0) return PNREF_ESHAPE;
+    const double scale = ldexp(1.0, -lg / 2);
+    for (int64_t b0 = 0; b0 < k; b0 += block) {
+        for (int64_t i = 0; i < block; ++i) {
+            double s = 0.0;
+            for (int64_t j = 0; j < block; ++j) {
+                const double v = (double)pnref_half_to_float(x[b0 + j]);
+                s += (__builtin_popcountll((uint64_t)(i & j)) & 1) ? -v : v;
+            }
+            out[b0 + i] = pnref_double_to_half(s * scale);  /* s starts at +0: an exact zero is +0 */
+        }
+    }
+    return PNREF_OK;
+}

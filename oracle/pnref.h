@@ -53,6 +53,16 @@ int pnref_gemm_f64(int type, const uint8_t *w, int64_t n, int64_t k,
 /* Signed-scale round-to-nearest quantizer: fp32 N x K -> packed rows. */
 int pnref_quantize(int type, const float *w, int64_t n, int64_t k, uint8_t *out);
 
+/* Blockwise Hadamard rotation of fp16 activations (tensorless, "How
+ * Qwen3.8-27B-PN3 uses it": the engine rotates the activations that reach the
+ * PN weights at run time; the page gives neither the size nor the scaling,
+ * readings in pnref.c):
+ *   out[b*B + i] = fp16_rne( sum_j H[i][j] x[b*B + j] / sqrt(B) ),
+ *   H[i][j] = (-1)^popcount(i & j)  (Sylvester order),
+ * for every block b of B = `block` elements; B a power of 4, k a multiple of
+ * B.  x and out hold fp16 bit patterns and may not overlap. */
+int pnref_rotate(const uint16_t *x, int64_t k, int64_t block, uint16_t *out);
+
 /* Threads the fp64 GEMV may use (OpenMP over rows); returns the count used. */
 int pnref_set_threads(int nthreads);
 

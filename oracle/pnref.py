@@ -12,6 +12,7 @@ from . import build as _build
 
 PN3T = 0
 PN4T = 1
+ROTATE_BLOCK = 1024  # Hadamard block of the activation rotation (reading in pnref.c)
 BLOCK_BYTES = 34
 _TYPES = {"pn3t": PN3T, "pn4t": PN4T, PN3T: PN3T, PN4T: PN4T}
 
@@ -60,6 +61,7 @@ class Oracle:
                                        ctypes.c_int, f64p, i64, f64p]
         lib.pnref_quantize.argtypes = [ctypes.c_int, f32p, i64, i64, u8p]
         lib.pnref_set_threads.argtypes = [ctypes.c_int]
+        lib.pnref_rotate.argtypes = [u16p, i64, i64, u16p]
         lib.pnref_weights_per_block.argtypes = [ctypes.c_int]
         lib.pnref_zero_point.argtypes = [ctypes.c_int]
         self.lib = lib
@@ -133,6 +135,18 @@ class Oracle:
                                        _ptr(a, ctypes.c_double)), "gemm_f64")
         return y, a
 
+    def rotate(self, x, block=ROTATE_BLOCK):
+        """Blockwise Hadamard rotation of fp16 rows: x fp16 [..., K] -> fp16
+        [..., K] (pnref_rotate on each row)."""
+        x = np.ascontiguousarray(x, dtype=np.float16)
+        k = x.shape[-1]
+        flat = x.reshape(-1, k).view(np.uint16)
+        out = np.empty_like(flat)
+        for r in range(flat.shape[0]):
+            _check(self.lib.pnref_rotate(_ptr(flat[r], ctypes.c_uint16), k, block,
+                                         _ptr(out[r], ctypes.c_uint16)), "rotate")
+        return out.view(np.float16).reshape(x.shape)
+
     def quantize(self, pn_type, wf, n, k):
         """Quantize fp32 [N, K] into packed PN rows (uint8 [N, row_bytes])."""
         wf = np.ascontiguousarray(wf, dtype=np.float32).reshape(n, k)
@@ -194,3 +208,7 @@ def gemm_f64(pn_type, w, n, k, xm):
 
 def quantize(pn_type, wf, n, k):
     return default().quantize(pn_type, wf, n, k)
+
+
+def rotate(x, block=ROTATE_BLOCK):
+    return default().rotate(x, block)

@@ -12,7 +12,10 @@ oracle disagrees with what the pages and the mathematics fix:
     sign"); decode is exact ("Exact decode in fp32"); the two 16-bit halves
     decode independently ("Codes never straddle the two halves of a word");
   - brute force: exact rational GEMV sums (fractions.Fraction) on tiny inputs
-    and an exhaustive nearest-code search for the quantizer.
+    and an exhaustive nearest-code search for the quantizer;
+  - the activation rotation: a case worked by hand, the closed-form columns
+    of the Sylvester matrix, scipy's Hadamard matrix with numpy's fp16
+    rounding, and length preservation.
 The same pins run against deliberately broken copies of the oracle in
 test_oracle_mutants.py, to show that a plausible mistake fails at least one.
 """
@@ -386,8 +389,90 @@ def pin_quantizer_edges(o):
         raise AssertionError("quantizer accepted a block whose scale overflows fp16")
 
 
+# ---------------------------------------------------------------------------
+# Hadamard rotation of the activations (tensorless, "How Qwen3.8-27B-PN3 uses
+# it"; block size, order and scale are readings, see pnref.c)
+# ---------------------------------------------------------------------------
+def _sylvester_sign(i, j):
+    return -1.0 if bin(i & j).count("1") & 1 else 1.0
+
+
+def pin_rotate_hand_worked(o):
+    """B = 4 worked by hand: H4 [1,2,3,4] / 2 = [10,-2,-4,0] / 2; zeros are +0."""
+    got = o.rotate(np.array([1, 2, 3, 4], np.float16), 4)
+    assert got.tolist() == [5.0, -1.0, -2.0, 0.0], got
+    assert not np.signbit(got[3])
+    got = o.rotate(np.array([-0.0, -0.0, -0.0, -0.0], np.float16), 4)
+    assert got.tolist() == [0.0] * 4 and not np.any(np.signbit(got)), got
+    # B = 16: x = e_5 * 4 -> column 5 of H16 (entries +-1), times 4 / 4
+    x = np.zeros(16, np.float16)
+    x[5] = 4.0
+    got = o.rotate(x, 16)
+    assert got.tolist() == [_sylvester_sign(i, 5) for i in range(16)], got
+
+
+def pin_rotate_unit_columns(o):
+    """Closed form: the rotation of 32 e_j is column j of the 1024 Sylvester
+    matrix, (-1)^popcount(i & j), and rotating it again gives 32 e_j back
+    (H / 32 is symmetric and orthogonal)."""
+    for j in (0, 1, 2, 3, 77, 512, 1000, 1023):
+        x = np.zeros(2048, np.float16)
+        x[1024 + j] = 32.0
+        got = o.rotate(x).astype(np.float64)
+        want = np.zeros(2048)
+        want[1024:] = [_sylvester_sign(i, j) for i in range(1024)]
+        assert np.array_equal(got, want), "column %d" % j
+        back = o.rotate(got.astype(np.float16))
+        assert np.array_equal(back.astype(np.float64), x.astype(np.float64)), "involution %d" % j
+
+
+def pin_rotate_library(o):
+    """Against scipy's Sylvester Hadamard matrix and numpy's fp16 rounding of
+    the fp64 product (exact here), for every block size the oracle takes:
+    N(0,1), wide-range and tie-prone inputs, results that overflow fp16 and
+    results that are fp16 subnormals."""
+    import scipy.linalg
+    rs = np.random.default_rng(11)
+    for b in (4, 16, 64, 256, 1024):
+        h = scipy.linalg.hadamard(b).astype(np.float64)
+        xs = [rs.standard_normal(4 * b),
+              rs.standard_normal(4 * b) * np.exp2(rs.integers(-20, 12, 4 * b)),
+              np.round(rs.standard_normal(4 * b) * 64) / 64 + np.exp2(-11.0),
+              np.full(4 * b, 60000.0),
+              rs.standard_normal(4 * b) * 2.0 ** -18]
+        for x in xs:
+            x = x.astype(np.float16)
+            exact = ((x.astype(np.float64).reshape(-1, b) @ h) / np.sqrt(b)).reshape(-1)
+            with np.errstate(over="ignore"):
+                want = exact.astype(np.float16)
+            # an exact zero is +0; a tiny negative value still rounds to -0
+            want = np.where(exact == 0, np.float16(0), want)
+            got = o.rotate(x, b)
+            assert np.array_equal(got.view(np.uint16), want.view(np.uint16)), "block %d" % b
+
+
+def pin_rotate_norm(o):
+    """Orthonormal: the rotated block keeps the vector's length, up to the
+    fp16 rounding of each output."""
+    rs = np.random.default_rng(12)
+    x = rs.standard_normal(5120).astype(np.float16)
+    got = o.rotate(x).astype(np.float64).reshape(5, 1024)
+    n0 = np.linalg.norm(x.astype(np.float64).reshape(5, 1024), axis=1)
+    assert np.allclose(np.linalg.norm(got, axis=1), n0, rtol=2.0 ** -10)
+
+
+def pin_rotate_rejects_shapes(o):
+    for k, b in ((1000, 1024), (1024, 512), (1024, 2048), (12, 3)):
+        try:
+            o.rotate(np.zeros(k, np.float16), b)
+        except ValueError:
+            continue
+        raise AssertionError("rotate took K=%d, block %d" % (k, b))
+
+
 ALL_PINS = [pin_half_to_float_all, pin_double_to_half, pin_closed_forms, pin_goldens,
             pin_golden_alignment, pin_range_and_zero, pin_halves_independent,
             pin_unused_bits_ignored, pin_one_hot_codes, pin_gemv_goldens, pin_gemv_exact,
             pin_gemv_special, pin_gemm_reduces_to_gemv, pin_quantizer_round_trip,
-            pin_quantizer_rules, pin_quantizer_edges]
+            pin_quantizer_rules, pin_quantizer_edges, pin_rotate_hand_worked,
+            pin_rotate_unit_columns, pin_rotate_library, pin_rotate_norm, pin_rotate_rejects_shapes]

@@ -33,6 +33,14 @@ MUTANTS = [
     ("quantizer rounds half up", "nearbyint((double)src[i] / d)", "floor((double)src[i] / d + 0.5)"),
     ("quantizer without clamp", "if (v > (double)((1 << b) - 1)) v = (double)((1 << b) - 1);", ""),
     ("half rounding truncates", "double q = nearbyint(ldexp(a, 10 - e));", "double q = floor(ldexp(a, 10 - e));"),
+    ("rotation sign flipped", "& 1) ? -v : v;", "& 1) ? v : -v;"),
+    ("rotation transposed index", "popcountll((uint64_t)(i & j))", "popcountll((uint64_t)(i | j))"),
+    ("rotation scale off", "ldexp(1.0, -lg / 2)", "ldexp(1.0, -lg / 2 + 1)"),
+    ("rotation block offset lost", "pnref_half_to_float(x[b0 + j])", "pnref_half_to_float(x[j])"),
+    ("rotation first term dropped", "for (int64_t j = 0; j < block; ++j) {\n                const double v",
+     "for (int64_t j = 1; j < block; ++j) {\n                const double v"),
+    ("rotation accumulates in fp32", "            double s = 0.0;\n            for (int64_t j = 0",
+     "            float s = 0.0f;\n            for (int64_t j = 0"),
 ]
 
 
