@@ -6,7 +6,7 @@ on one MI355X.
 A step is one token: every one of the 448 GEMVs, each with its own fp16
 input, all inputs resident in HBM before timing starts.  Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--schedule token|layer|gemv]
+  python bench.py [--steps K] [--warmup W] [--schedule token|layer|gemv|token_rot]
                   [--config 3|4] [--math mfma|valu] [--no-cpu-baseline]
 
 --config 4 runs the same sweep with M = 8 activation rows per matrix (the
@@ -174,7 +174,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--schedule", default="token", choices=["token", "layer", "gemv"])
+    ap.add_argument("--schedule", default="token", choices=["token", "layer", "gemv", "token_rot"])
     ap.add_argument("--config", type=int, default=3, choices=[3, 4])
     ap.add_argument("--math", default="mfma", choices=["mfma", "valu"],
                     help="small-batch arithmetic (--config 4)")
@@ -287,7 +287,7 @@ def main():
     secondary = {}
     if not args.no_secondary:
         if m is None:
-            others = [(o, None) for o in ("layer", "gemv") if o != schedule]
+            others = [(o, None) for o in ("layer", "gemv", "token_rot") if o != schedule]
         else:
             other_math = "valu" if args.math == "mfma" else "mfma"
             others = [(o, args.math) for o in ("token", "gemv") if o != schedule] + [(schedule, other_math)]
@@ -300,6 +300,10 @@ def main():
             secondary[key] = {"tokens_per_s": round(args.steps / w2, 2),
                               "gbps": round(bytes_per_token / (w2 / args.steps) / 1e9, 1),
                               "launches_per_token": sw.launches(other), "variant": var2}
+            if other == "token_rot":
+                secondary[key]["ms_per_token"] = round(w2 / args.steps * 1e3, 4)
+                secondary[key]["note"] = ("inputs in the unrotated basis: one Hadamard rotation launch over "
+                                          "all 448 inputs, then the token launch")
             log("schedule %s: %.1f tok/s" % (key, args.steps / w2))
         if m is not None:
             B.pn_set_smallm_math(args.math)

@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpn.so")
 # Every symbol include/pn.h declares.
 EXPORTS = ("pn_weights_per_block", "pn_row_bytes", "pn_gemv", "pn_gemv2",
            "pn_gemm_smallm", "pn_set_smallm_math", "pn_get_smallm_math", "pn_set_gemv_kernel",
-           "pn_get_gemv_kernel", "pn_dequantize",
+           "pn_get_gemv_kernel", "pn_dequantize", "pn_rotate",
            "pn_group_create", "pn_group_create_smallm", "pn_group_run", "pn_group_destroy",
            "pn_read_probe_scratch_bytes", "pn_read_probe", "pn_status_str", "pn_last_variant",
            "pn_variant_name")
@@ -42,7 +42,11 @@ class PNError(RuntimeError):
 class pn_gemv_desc(ctypes.Structure):
     _fields_ = [("W", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
                 ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("type", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("flags", ctypes.c_int32)]
+
+
+DESC_ROTATE = 1  # PN_DESC_ROTATE
+ROTATE_BLOCK = 1024  # PN_ROTATE_BLOCK
 
 
 class pn_gemm_desc(ctypes.Structure):
@@ -86,6 +90,8 @@ def lib():
     L.pn_group_create_smallm.restype = i32
     L.pn_dequantize.argtypes = [i32, vp, i64, i64, vp, vp]
     L.pn_dequantize.restype = i32
+    L.pn_rotate.argtypes = [vp, i64, i32, i64, vp, i64, vp]
+    L.pn_rotate.restype = i32
     L.pn_group_create.argtypes = [ctypes.POINTER(pn_gemv_desc), i32, ctypes.POINTER(vp)]
     L.pn_group_create.restype = i32
     L.pn_group_run.argtypes = [vp, vp]
@@ -199,12 +205,20 @@ def pn_dequantize(pn_type, W, N, K, out, stream=None, check=True):
     return st
 
 
+def pn_rotate(x, K, M, ldx, out, ldo, stream=None, check=True):
+    st = lib().pn_rotate(_ptr(x), K, M, ldx, _ptr(out), ldo, _stream(stream))
+    if check:
+        _check(st, "pn_rotate")
+    return st
+
+
 class Group:
     """A pn_group plan over (pn_type, W, N, K, x, y) problems; frees itself.
     With smallm=True the problems are (pn_type, W, N, K, X, ldx, M, Y, ldy)
-    and the plan comes from pn_group_create_smallm."""
+    and the plan comes from pn_group_create_smallm.  `rotate` (GEMV plans):
+    one flag per problem, or one for all, for PN_DESC_ROTATE."""
 
-    def __init__(self, problems, smallm=False):
+    def __init__(self, problems, smallm=False, rotate=False):
         h = ctypes.c_void_p()
         if smallm:
             arr = (pn_gemm_desc * len(problems))()
@@ -214,8 +228,10 @@ class Group:
                    "pn_group_create_smallm")
         else:
             arr = (pn_gemv_desc * len(problems))()
+            flags = list(rotate) if isinstance(rotate, (list, tuple)) else [rotate] * len(problems)
             for i, (t, W, N, K, x, y) in enumerate(problems):
-                arr[i] = pn_gemv_desc(_ptr(W), _ptr(x), _ptr(y), N, K, _t(t), 0)
+                arr[i] = pn_gemv_desc(_ptr(W), _ptr(x), _ptr(y), N, K, _t(t),
+                                      DESC_ROTATE if flags[i] else 0)
             _check(lib().pn_group_create(arr, len(problems), ctypes.byref(h)), "pn_group_create")
         self.handle = h
         self.keep = problems  # the plan holds raw device pointers

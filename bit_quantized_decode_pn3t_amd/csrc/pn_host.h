@@ -24,6 +24,7 @@ enum Variant {
     kVarGroupSmallMMfma = 8,
     kVarRows = 9,
     kVarGroupRows = 10,
+    kVarRotate = 11,
 };
 
 extern thread_local int g_last_variant;
@@ -58,6 +59,8 @@ struct pn_group {
     int total_tiles;    // tiles (gemv_stream, gemm_stream) or waves (gemv_rows)
     int lds;            // dynamic LDS bytes of the launch
     int flags;          // kind-specific launch choice
+    void *rot;          // problems with rotated inputs: RotJob list, then the rotated copies
+    int rot_jobs;       // 1024-element blocks to rotate before the GEMV launch (0: none)
 };
 
 namespace pn {
@@ -74,5 +77,12 @@ pn_status rows_launch(int t, const void *W0, const void *W1, int64_t N, int64_t 
                       float *y1, hipStream_t s);
 pn_status rows_group_create(const pn_gemv_desc *descs, int count, pn_group **out);
 pn_status rows_group_run(const pn_group *g, hipStream_t s);
+// One block of a plan's activation rotation (pn_rotate.hip): src rotated
+// into dst, PN_ROTATE_BLOCK fp16 elements each.
+struct RotJob {
+    const uint16_t *src;
+    uint16_t *dst;
+};
+pn_status rotate_jobs_launch(const RotJob *jobs, int total, hipStream_t s);
 }  // namespace host
 }  // namespace pn

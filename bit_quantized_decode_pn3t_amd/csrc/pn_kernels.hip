@@ -625,10 +625,11 @@ pn_status pn_dequantize(pn_type t, const void *W, int64_t N, int64_t K, float *o
     return PN_OK;
 }
 
-pn_status pn_group_create(const pn_gemv_desc *descs, int count, pn_group **out)
+namespace {
+
+// The plan for problems whose x is used as given.
+pn_status group_create_plain(const pn_gemv_desc *descs, int count, pn_group **out)
 {
-    if (!descs || !out || count < 1) return PN_EINVAL;
-    *out = nullptr;
     Prob *host = (Prob *)calloc((size_t)count, sizeof(Prob));
     if (!host) return PN_ENOMEM;
     int lds = 0;
@@ -693,9 +694,75 @@ pn_status pn_group_create(const pn_gemv_desc *descs, int count, pn_group **out)
     return PN_OK;
 }
 
+}  // namespace
+
+// Problems flagged PN_DESC_ROTATE get a plan-owned copy of x, rotated at the
+// start of every run (one launch over all their 1024-element blocks); the
+// GEMV plan is built on descriptors that point at the copies.
+pn_status pn_group_create(const pn_gemv_desc *descs, int count, pn_group **out)
+{
+    if (!descs || !out || count < 1) return PN_EINVAL;
+    *out = nullptr;
+    int64_t rot_elems = 0, rot_jobs = 0;
+    for (int i = 0; i < count; ++i) {
+        const pn_gemv_desc &e = descs[i];
+        if (e.flags & ~PN_DESC_ROTATE) return PN_EINVAL;
+        if (!(e.flags & PN_DESC_ROTATE)) continue;
+        if (!e.x) return PN_EINVAL;
+        if (e.K < PN_ROTATE_BLOCK || e.K % PN_ROTATE_BLOCK != 0) return PN_ESHAPE;
+        if (!aligned4(e.x)) return PN_EALIGN;
+        rot_elems += e.K;
+        rot_jobs += e.K / PN_ROTATE_BLOCK;
+    }
+    if (rot_jobs == 0) return group_create_plain(descs, count, out);
+    if (rot_jobs > INT32_MAX / 2) return PN_EUNSUPPORTED;
+    const size_t jbytes = ((size_t)rot_jobs * sizeof(RotJob) + 4095) & ~(size_t)4095;
+    void *dev = nullptr;
+    if (hipMalloc(&dev, jbytes + (size_t)rot_elems * sizeof(uint16_t)) != hipSuccess) return PN_ENOMEM;
+    pn_gemv_desc *d2 = (pn_gemv_desc *)malloc(sizeof(pn_gemv_desc) * (size_t)count);
+    RotJob *jobs = (RotJob *)malloc(sizeof(RotJob) * (size_t)rot_jobs);
+    if (!d2 || !jobs) {
+        free(d2);
+        free(jobs);
+        (void)hipFree(dev);
+        return PN_ENOMEM;
+    }
+    uint16_t *copies = (uint16_t *)((uint8_t *)dev + jbytes);  // 4 KiB aligned, 2 KiB per block
+    int64_t off = 0, j = 0;
+    for (int i = 0; i < count; ++i) {
+        d2[i] = descs[i];
+        d2[i].flags = 0;
+        if (!(descs[i].flags & PN_DESC_ROTATE)) continue;
+        const uint16_t *src = (const uint16_t *)descs[i].x;
+        for (int64_t b = 0; b < descs[i].K / PN_ROTATE_BLOCK; ++b, ++j) {
+            jobs[j].src = src + b * PN_ROTATE_BLOCK;
+            jobs[j].dst = copies + off + b * PN_ROTATE_BLOCK;
+        }
+        d2[i].x = copies + off;
+        off += descs[i].K;
+    }
+    pn_status st = hipMemcpy(dev, jobs, sizeof(RotJob) * (size_t)rot_jobs, hipMemcpyHostToDevice) == hipSuccess
+                       ? PN_OK
+                       : PN_ELAUNCH;
+    if (st == PN_OK) st = group_create_plain(d2, count, out);
+    free(d2);
+    free(jobs);
+    if (st != PN_OK) {
+        (void)hipFree(dev);
+        return st;
+    }
+    (*out)->rot = dev;
+    (*out)->rot_jobs = (int)rot_jobs;
+    return PN_OK;
+}
+
 pn_status pn_group_run(const pn_group *g, void *stream)
 {
     if (!g) return PN_EINVAL;
+    if (g->rot_jobs > 0) {
+        const pn_status st = rotate_jobs_launch((const RotJob *)g->rot, g->rot_jobs, (hipStream_t)stream);
+        if (st != PN_OK) return st;
+    }
     if (g->kind == kGroupSmallM) return smallm_group_run(g, (hipStream_t)stream);
     if (g->kind == kGroupGemvRows) return rows_group_run(g, (hipStream_t)stream);
     StreamArgs a;
@@ -711,6 +778,7 @@ void pn_group_destroy(pn_group *g)
     if (!g) return;
     (void)hipDeviceSynchronize();
     (void)hipFree(g->table);
+    if (g->rot) (void)hipFree(g->rot);
     free(g);
 }
 
@@ -742,6 +810,7 @@ const char *pn_variant_name(int v)
     case kVarGroupSmallMMfma: return "gemm_stream_mfma_group";
     case kVarRows: return "gemv_rows";
     case kVarGroupRows: return "gemv_rows_group";
+    case kVarRotate: return "hadamard_rotate";
     case kVarDequant: return "dequant";
     case kVarGroupStream: return "gemv_stream_group";
     }

@@ -8,7 +8,10 @@ GEMVs on the current stream in one of these launch schedules:
   token  one grouped launch for all GEMVs of the token (pn_group_run);
   layer  four launches per layer, the groups a real decoder can form because
          their inputs are ready together: {q, k, v}, {o}, {gate, up}, {down};
-  gemv   one pn_gemv launch per matrix.
+  gemv   one pn_gemv launch per matrix;
+  token_rot  the token plan with every input in the model's unrotated basis
+         (PN_DESC_ROTATE: one rotation launch over all inputs, then the
+         grouped GEMV launch).
 With M > 1 the token schedule is one pn_group_create_smallm plan and the gemv
 schedule one pn_gemm_smallm launch per matrix.  A schedule can be captured
 once into a HIP graph (torch.cuda.CUDAGraph) and replayed.
@@ -63,6 +66,10 @@ class Sweep:
         if schedule == "token" and "token" not in self.groups:
             self.groups["token"] = [B.Group([self._problem(e) for e in self.mats],
                                             smallm=self.m is not None)]
+        if schedule == "token_rot" and "token_rot" not in self.groups:
+            if self.m is not None:
+                raise ValueError("rotated inputs: M = 1 plans only")
+            self.groups["token_rot"] = [B.Group([self._problem(e) for e in self.mats], rotate=True)]
         if schedule == "layer" and "layer" not in self.groups:
             gl = []
             per = len(synth.SWEEP_LAYER)
@@ -72,13 +79,15 @@ class Sweep:
             self.groups["layer"] = gl
 
     def launches(self, schedule):
+        if schedule == "token_rot":
+            return 2
         if schedule in ("token", "layer"):
             return len(self.groups[schedule])
         return len(self.mats)
 
     def step(self, schedule="layer"):
         """Enqueue one token's GEMVs on the current stream."""
-        if schedule in ("token", "layer"):
+        if schedule in ("token", "layer", "token_rot"):
             self.prepare(schedule)
             for g in self.groups[schedule]:
                 g.run()
@@ -95,7 +104,7 @@ class Sweep:
 
     def capture(self, schedule="layer"):
         """Capture one step into a HIP graph; returns the graph."""
-        if schedule in ("token", "layer"):
+        if schedule in ("token", "layer", "token_rot"):
             self.prepare(schedule)
         self.step(schedule)  # warm: first launches, occupancy queries
         torch.cuda.synchronize()

@@ -133,6 +133,25 @@ pn_gemv_kernel pn_get_gemv_kernel(void);
 pn_status pn_dequantize(pn_type t, const void *W, int64_t N, int64_t K,
                         float *out, void *stream);
 
+/* Blockwise Hadamard rotation of fp16 activations (tensorless, "How
+ * Qwen3.8-27B-PN3 uses it": the model's engine rotates the activations that
+ * reach the PN weights at run time; the page gives no size or scale, and
+ * the reading here is the one the CPU oracle fixes):
+ *   out[m*ldo + b*1024 + i] =
+ *       fp16_rne( sum_j H[i][j] x[m*ldx + b*1024 + j] / 32 ),
+ *   H[i][j] = (-1)^popcount(i & j)   (Sylvester order, 1024 x 1024),
+ * for every row m < M and every 1024-element block b of the K columns.
+ * Exact up to the one fp16 rounding (ties to even; an exact zero is +0), so
+ * every correct implementation gives the same bits.
+ *   x, out : fp16, device, 4-byte aligned, ldx and ldo even and >= K.
+ *            out may be x (same ld): rotation in place.  Other overlaps are
+ *            not allowed.
+ *   K      : a multiple of 1024 (else PN_ESHAPE); M >= 1.
+ * Enqueued on `stream`; returns without waiting. */
+#define PN_ROTATE_BLOCK 1024
+pn_status pn_rotate(const uint16_t *x, int64_t K, int M, int64_t ldx,
+                    uint16_t *out, int64_t ldo, void *stream);
+
 /* A group of independent GEMVs run by one kernel launch (a decoder layer's
  * projections, or a whole per-token weight sweep).  Each entry is one
  * pn_gemv problem; the entries may mix types and shapes. */
@@ -143,14 +162,20 @@ typedef struct pn_gemv_desc {
     int64_t N;
     int64_t K;
     int32_t type;    /* pn_type                      */
-    int32_t reserved;
+    int32_t flags;   /* 0, or PN_DESC_ROTATE         */
 } pn_gemv_desc;
+
+/* Entry flag: x is in the model's unrotated basis; the plan multiplies by
+ * pn_rotate's image of x (y = W H x).  Needs K a multiple of 1024.  The plan
+ * keeps a device copy of each such x, rotated at the start of every run by
+ * one extra launch ahead of the GEMV launch, on the same stream. */
+#define PN_DESC_ROTATE 1
 
 typedef struct pn_group pn_group;
 
 /* Validate `count` descriptors (host array) and build a launch plan.  This
- * call allocates device memory for the plan's tables and copies them there
- * synchronously; the plan holds the descriptors' device pointers, which must
+ * call allocates device memory for the plan's tables (and for the rotated
+ * copies of PN_DESC_ROTATE inputs) and copies them there synchronously; the plan holds the descriptors' device pointers, which must
  * stay valid while the plan is used.  Returns PN_ENOMEM if allocation fails.
  * The plan runs on the row-tile kernel if that takes every problem and the
  * launch (see pn_set_gemv_kernel); otherwise every problem's rows must be

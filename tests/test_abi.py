@@ -95,6 +95,28 @@ def test_group_host_checks():
     lib.pn_group_destroy(None)
 
 
+def test_rotate_host_checks():
+    lib = B.lib()
+    assert lib.pn_rotate(None, 1024, 1, 1024, FAKE, 1024, None) == PN_EINVAL
+    assert lib.pn_rotate(FAKE, 1024, 1, 1024, None, 1024, None) == PN_EINVAL
+    for k, m, ldx, ldo in ((1000, 1, 1000, 1000), (512, 1, 512, 512), (0, 1, 0, 0), (1024, 0, 1024, 1024),
+                           (1024, 1, 1023, 1024), (2048, 2, 2048, 1024)):
+        assert lib.pn_rotate(FAKE, k, m, ldx, FAKE, ldo, None) == PN_ESHAPE, (k, m, ldx, ldo)
+    assert lib.pn_rotate(FAKE + 2, 1024, 1, 1024, FAKE, 1024, None) == PN_EALIGN
+    assert lib.pn_rotate(FAKE, 1024, 2, 1026, FAKE + 2, 1025, None) == PN_EALIGN
+    # group entries: unknown flag bits, and rotation of K not a multiple of 1024
+    arr = (B.pn_gemv_desc * 1)()
+    arr[0] = B.pn_gemv_desc(FAKE, FAKE, FAKE, 4, 5120, 0, 2)
+    h = ctypes.c_void_p()
+    assert lib.pn_group_create(arr, 1, ctypes.byref(h)) == PN_EINVAL
+    with pytest.raises(B.PNError) as e:
+        B.Group([("pn3t", FAKE, 4, 640, FAKE, FAKE)], rotate=True)
+    assert e.value.status == PN_ESHAPE
+    with pytest.raises(B.PNError) as e:
+        B.Group([("pn3t", FAKE, 4, 5120, FAKE + 2, FAKE)], rotate=True)
+    assert e.value.status == PN_EALIGN
+
+
 def test_smallm_group_host_checks():
     ok = ("pn3t", FAKE, 4, 80, FAKE, 80, 2, FAKE, 4)
     bad = [

@@ -18,14 +18,15 @@ from oracle import pnref  # noqa: E402
 ROWS = 6
 
 
-def _check_samples(sw, store, m=None):
+def _check_samples(sw, store, m=None, rotated=False):
     outs = {(e["layer"], e["mat"]): e["y"].cpu().numpy() for e in sw.mats}
     worst = 0.0
     for key, smp in store.items():
         y = outs[key]
         n_rows = len(smp["rows"])
         if m is None:
-            y64, a = pnref.gemv_f64(smp["type"], smp["W"], n_rows, smp["K"], smp["x"])
+            x = pnref.rotate(smp["x"]) if rotated else smp["x"]
+            y64, a = pnref.gemv_f64(smp["type"], smp["W"], n_rows, smp["K"], x)
             worst = max(worst, assert_gemv_close(y[smp["rows"]], y64, a, "sweep %s" % (key,)))
         else:
             y64, a = pnref.gemm_f64(smp["type"], smp["W"], n_rows, smp["K"], smp["x"])
@@ -47,7 +48,7 @@ def sweep_m1():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("schedule", ["layer", "token", "gemv"])
+@pytest.mark.parametrize("schedule", ["layer", "token", "gemv", "token_rot"])
 def test_sweep_m1(sweep_m1, schedule):
     sw, store = sweep_m1
     for e in sw.mats:
@@ -55,7 +56,7 @@ def test_sweep_m1(sweep_m1, schedule):
     say("sweep M=1 schedule %s" % schedule)
     sw.step(schedule)
     sync()
-    worst = _check_samples(sw, store)
+    worst = _check_samples(sw, store, rotated=schedule == "token_rot")
     say("sweep M=1 %s: worst |y-y64|/sum|wx| = %.3g" % (schedule, worst))
 
 
