@@ -28,12 +28,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "PN GEMV achieved HBM GB/s (% of peak) + 27B-shaped layer-sweep tokens/s"
 PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
-# Sources of the kernel each workload times (M = 1: gemv_rows for the
-# one-launch sweep, gemv_stream for smaller launches; M > 1: gemm_stream):
-# the committed counters are valid for one hash of these.
+# Sources of the kernel each counted workload times (the M = 1 one-launch
+# sweep: gemv_rows; M > 1: gemm_stream): the committed counters are valid for
+# one hash of these.
 KERNEL_SOURCES = {
-    "m1": ["bit_quantized_decode_pn3t_amd/csrc/pn_kernels.hip",
-           "bit_quantized_decode_pn3t_amd/csrc/pn_gemv_rows.hip",
+    "m1": ["bit_quantized_decode_pn3t_amd/csrc/pn_gemv_rows.hip",
            "bit_quantized_decode_pn3t_amd/csrc/pn_device.h"],
     "smallm": ["bit_quantized_decode_pn3t_amd/csrc/pn_smallm.hip",
                "bit_quantized_decode_pn3t_amd/csrc/pn_device.h"],
