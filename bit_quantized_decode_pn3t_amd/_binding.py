@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpn.so")
 # Every symbol include/pn.h declares.
 EXPORTS = ("pn_weights_per_block", "pn_row_bytes", "pn_gemv", "pn_gemv2",
            "pn_gemm_smallm", "pn_set_smallm_math", "pn_get_smallm_math", "pn_set_gemv_kernel",
-           "pn_get_gemv_kernel", "pn_dequantize", "pn_rotate",
+           "pn_get_gemv_kernel", "pn_dequantize", "pn_rotate", "pn_gemm_prefill",
            "pn_group_create", "pn_group_create_smallm", "pn_group_run", "pn_group_destroy",
            "pn_read_probe_scratch_bytes", "pn_read_probe", "pn_status_str", "pn_last_variant",
            "pn_variant_name")
@@ -92,6 +92,8 @@ def lib():
     L.pn_dequantize.restype = i32
     L.pn_rotate.argtypes = [vp, i64, i32, i64, vp, i64, vp]
     L.pn_rotate.restype = i32
+    L.pn_gemm_prefill.argtypes = [i32, vp, i64, i64, vp, i64, i64, vp, i64, vp]
+    L.pn_gemm_prefill.restype = i32
     L.pn_group_create.argtypes = [ctypes.POINTER(pn_gemv_desc), i32, ctypes.POINTER(vp)]
     L.pn_group_create.restype = i32
     L.pn_group_run.argtypes = [vp, vp]
@@ -202,6 +204,13 @@ def pn_dequantize(pn_type, W, N, K, out, stream=None, check=True):
     st = lib().pn_dequantize(_t(pn_type), _ptr(W), N, K, _ptr(out), _stream(stream))
     if check:
         _check(st, "pn_dequantize")
+    return st
+
+
+def pn_gemm_prefill(pn_type, W, N, K, X, ldx, M, Y, ldy, stream=None, check=True):
+    st = lib().pn_gemm_prefill(_t(pn_type), _ptr(W), N, K, _ptr(X), ldx, M, _ptr(Y), ldy, _stream(stream))
+    if check:
+        _check(st, "pn_gemm_prefill")
     return st
 
 

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libpn.so")
 SOURCES = [os.path.join(HERE, "csrc", n) for n in ("pn_kernels.hip", "pn_gemv_rows.hip", "pn_smallm.hip", "pn_probe.hip",
-                                                               "pn_rotate.hip")]
+                                                               "pn_rotate.hip", "pn_prefill.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -25,6 +25,7 @@ enum Variant {
     kVarRows = 9,
     kVarGroupRows = 10,
     kVarRotate = 11,
+    kVarPrefill = 12,
 };
 
 extern thread_local int g_last_variant;

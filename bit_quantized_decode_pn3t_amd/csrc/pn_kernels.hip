@@ -811,6 +811,7 @@ const char *pn_variant_name(int v)
     case kVarRows: return "gemv_rows";
     case kVarGroupRows: return "gemv_rows_group";
     case kVarRotate: return "hadamard_rotate";
+    case kVarPrefill: return "gemm_prefill";
     case kVarDequant: return "dequant";
     case kVarGroupStream: return "gemv_stream_group";
     }

@@ -1,0 +1,247 @@
+// pn_prefill.hip - PN GEMM for prefill (any number of activation rows), for
+// AMD Instinct MI355X (gfx950), and its C ABI: pn_gemm_prefill.
+//
+// Y[m, r] = sum_k w[r, k] X[m, k] for m < M, w = d * (n - z) ("Exact decode
+// in fp32").  The pages' engine handles prefill by dequantizing PN weights
+// for a chunked GEMM ("What the fork adds"); here the weights are decoded
+// inside the GEMM, from the packed bytes, and never written out: at prompt
+// lengths of hundreds of tokens a GEMM that re-read a decoded fp16 copy
+// would move 2 bytes a weight per pass instead of 0.43-0.53.
+//
+// Products on MFMA (v_mfma_f32_32x32x16_f16): X is the A operand, the
+// decoded weights (n - z) - small integers, exact in fp16 - the B operand.
+// d * (n - z) is not always exact in fp16 (up to 14 significant bits), so d
+// stays out of the operands: each 34-byte block's products go into a fresh
+// accumulator, which is then scaled by that block's d in fp32 and added to
+// the running sum.
+//
+// Tiles.  A workgroup of four waves computes 128 rows of X (M) by 128
+// weight rows (N); wave (wm, wn) owns the 64 x 64 sub-tile of 2 x 2 MFMA
+// tiles.  The K loop takes one block pair (two 34-byte blocks, 68 bytes,
+// 17 aligned dwords: 160 k for pn3t, 128 for pn4t) at a time: the
+// workgroup stages the X tile (128 x 160 or 128 fp16) and the 128 rows'
+// block pairs in LDS with coalesced loads, and each wave decodes its 64
+// weight rows straight into B operands.
+//
+// Operand layouts (checked on the GPU: lane l of the 32 x 32 x 16 MFMA):
+// A row l % 32, k = 8 (l / 32) + e; B column l % 32, same k; result
+// register v holds row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.  So a
+// lane's 16 results share one weight row and one scale.
+//   pn4t  word j of a block holds codes 8j .. 8j + 7, so k-step s of a block
+//         takes word 2s + h in lane half h, and X at 64 b + 16 s + 8 h + e.
+//   pn3t  a word holds 10 codes, which do not fall on the 8-code grid; the
+//         k order inside a block is permuted instead (a GEMM's sum is
+//         order-free if A and B agree): lane half h takes words 4h .. 4h+3,
+//         and k-step s takes code pair s of each of them; X is read at the
+//         same permuted positions 80 b + 40 h + 10 j + 2 s + {0, 1}.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "pn_device.h"
+#include "pn_host.h"
+
+using namespace pn;
+using namespace pn::host;
+
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kPfThreads = 256;  // four waves
+constexpr int kPfM = 128;        // X rows per workgroup
+constexpr int kPfN = 128;        // weight rows per workgroup
+constexpr int kPfPad = 8;        // fp16 of padding per X row in LDS
+constexpr int kPairDw = 17;      // dwords per block pair
+
+template <int TYPE>
+struct Pf {
+    static constexpr int KS = TYPE == 0 ? 160 : 128;  // k per block pair
+    static constexpr int BK = KS / 2;                 // k per block
+    static constexpr int STEPS = BK / 16;             // MFMA k-steps per block
+    static constexpr int XROW = KS + kPfPad;          // fp16 per X row in LDS
+    static constexpr int XCH = KS / 8;                // 16-byte chunks per X row
+    static constexpr int XBYTES = kPfM * XROW * 2;
+    static constexpr int LDS = XBYTES + kPfN * kPairDw * 4;
+};
+
+struct PfArgs {
+    const uint8_t *W;  // packed rows
+    const uint16_t *X;
+    float *Y;
+    int64_t ldx, ldy;
+    int32_t N, M, S, pairs;  // S: row bytes; pairs: block pairs per row
+};
+
+__device__ __forceinline__ half8_t cat4(half2_t a, half2_t b, half2_t c, half2_t d)
+{
+    return __builtin_shufflevector(__builtin_shufflevector(a, b, 0, 1, 2, 3), __builtin_shufflevector(c, d, 0, 1, 2, 3),
+                                   0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Word j of block b of a staged block pair (17 dwords from LDS at p): the
+// first block's words are two bytes off the dword grid.
+__device__ __forceinline__ uint32_t pair_word(const uint32_t *p, int b, int j)
+{
+    return b == 0 ? __builtin_amdgcn_alignbit(p[j + 1], p[j], 16) : p[9 + j];
+}
+
+__device__ __forceinline__ float pair_scale(const uint32_t *p, int b)
+{
+    return half_bits_to_float(b == 0 ? p[0] & 0xffffu : p[8] >> 16);
+}
+
+template <int TYPE>
+__global__ __launch_bounds__(kPfThreads) void gemm_prefill(PfArgs a)
+{
+    using C = Pf<TYPE>;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    uint16_t *xs = (uint16_t *)lds;
+    uint32_t *ws = (uint32_t *)(lds + C::XBYTES);
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int h = lane >> 5, c = lane & 31;
+    const int n0 = blockIdx.x * kPfN, m0 = blockIdx.y * kPfM;
+
+    float16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = (float16_t){};
+
+    for (int p = 0; p < a.pairs; ++p) {
+        __syncthreads();  // the previous pair's reads are done
+        for (int i = threadIdx.x; i < kPfM * C::XCH; i += kPfThreads) {
+            const int r = i / C::XCH, ch = i - r * C::XCH;
+            const int m = m0 + r;
+            u32x4 v = (u32x4){0u, 0u, 0u, 0u};
+            if (m < a.M) v = *(const u32x4 *)(a.X + (int64_t)m * a.ldx + (int64_t)p * C::KS + 8 * ch);
+            *(u32x4 *)(xs + r * C::XROW + 8 * ch) = v;
+        }
+        for (int i = threadIdx.x; i < kPfN * kPairDw; i += kPfThreads) {
+            const int r = i / kPairDw, d = i - r * kPairDw;
+            const int n = n0 + r;
+            uint32_t v = 0u;
+            if (n < a.N) v = *(const uint32_t *)(a.W + (int64_t)n * a.S + 68 * (int64_t)p + 4 * d);
+            ws[r * kPairDw + d] = v;
+        }
+        __syncthreads();
+
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            // decode: the lane's four words of block b, for its row of each N tile
+            half2_t u[2][4][TYPE == 0 ? 5 : 4];
+            float d[2];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const uint32_t *pw = ws + (wn * 64 + nt * 32 + c) * kPairDw;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    Unpack<TYPE>::run(pair_word(pw, b, TYPE == 0 ? 4 * h + j : h + 2 * j), u[nt][j]);
+                d[nt] = pair_scale(pw, b);
+            }
+            float16_t P[2][2];  // the block's fresh accumulators
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) P[mt][nt] = (float16_t){};
+#pragma unroll
+            for (int s = 0; s < C::STEPS; ++s) {
+                half8_t B[2];
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    if constexpr (TYPE == 0)
+                        B[nt] = cat4(u[nt][0][s], u[nt][1][s], u[nt][2][s], u[nt][3][s]);
+                    else
+                        B[nt] = cat4(u[nt][s][0], u[nt][s][1], u[nt][s][2], u[nt][s][3]);
+                }
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    const uint16_t *px = xs + (wm * 64 + mt * 32 + c) * C::XROW;
+                    half8_t A;
+                    if constexpr (TYPE == 0) {
+                        const int k = 80 * b + 40 * h + 2 * s;
+                        A = cat4(as_half2(*(const uint32_t *)(px + k)), as_half2(*(const uint32_t *)(px + k + 10)),
+                                 as_half2(*(const uint32_t *)(px + k + 20)),
+                                 as_half2(*(const uint32_t *)(px + k + 30)));
+                    } else {
+                        A = __builtin_bit_cast(half8_t, *(const u32x4 *)(px + 64 * b + 16 * s + 8 * h));
+                    }
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt)
+                        P[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B[nt], P[mt][nt], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[mt][nt][v] = __builtin_fmaf(d[nt], P[mt][nt][v], acc[mt][nt][v]);
+        }
+    }
+
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const int n = n0 + wn * 64 + nt * 32 + c;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int m = m0 + wm * 64 + mt * 32 + 8 * (v / 4) + 4 * h + (v % 4);
+                if (m < a.M && n < a.N) a.Y[(int64_t)m * a.ldy + n] = acc[mt][nt][v];
+            }
+        }
+}
+
+bool set_prefill_attr()
+{
+    static int done = 0;
+    if (!done) {
+        if (hipFuncSetAttribute((const void *)gemm_prefill<0>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                Pf<0>::LDS) != hipSuccess ||
+            hipFuncSetAttribute((const void *)gemm_prefill<1>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                Pf<1>::LDS) != hipSuccess)
+            return false;
+        done = 1;
+    }
+    return true;
+}
+
+}  // namespace
+
+pn_status pn_gemm_prefill(pn_type t, const void *W, int64_t N, int64_t K, const uint16_t *X, int64_t ldx, int64_t M,
+                          float *Y, int64_t ldy, void *stream)
+{
+    pn_status st = check_matrix(t, W, N, K);
+    if (st) return st;
+    if (!X || !Y) return PN_EINVAL;
+    if (M < 1 || ldx < K || ldy < N) return PN_ESHAPE;
+    const int64_t nb = K / wpb(t);
+    if (nb % 2 != 0) return PN_EUNSUPPORTED;  // whole block pairs only
+    if (((uintptr_t)W & 3) || ((uintptr_t)X & 15) || (ldx & 7) || !aligned4(Y)) return PN_EALIGN;
+    if (M > INT32_MAX - kPfM || (M + kPfM - 1) / kPfM > 65535) return PN_EUNSUPPORTED;
+    if (!set_prefill_attr()) return PN_ELAUNCH;
+    PfArgs a;
+    a.W = (const uint8_t *)W;
+    a.X = X;
+    a.Y = Y;
+    a.ldx = ldx;
+    a.ldy = ldy;
+    a.N = (int32_t)N;
+    a.M = (int32_t)M;
+    a.S = (int32_t)(nb * 34);
+    a.pairs = (int32_t)(nb / 2);
+    const dim3 grid((unsigned)((N + kPfN - 1) / kPfN), (unsigned)((M + kPfM - 1) / kPfM));
+    const hipStream_t s = (hipStream_t)stream;
+    if (t == PN_PN3T)
+        hipLaunchKernelGGL(gemm_prefill<0>, grid, dim3(kPfThreads), Pf<0>::LDS, s, a);
+    else
+        hipLaunchKernelGGL(gemm_prefill<1>, grid, dim3(kPfThreads), Pf<1>::LDS, s, a);
+    if (hipGetLastError() != hipSuccess) return PN_ELAUNCH;
+    g_last_variant = kVarPrefill;
+    return PN_OK;
+}

@@ -92,6 +92,23 @@ pn_status pn_gemm_smallm(pn_type t, const void *W, int64_t N, int64_t K,
                          const void *X, int64_t ldx, int M,
                          float *Y, int64_t ldy, void *stream);
 
+/* Prefill: the same product for any number of activation rows (a prompt's
+ * tokens),
+ *   Y[m*ldy + r] = sum_k w[r,k] X[m*ldx + k],  m < M,  w = d * (n - z),
+ * with the weights decoded inside the GEMM from the packed rows and never
+ * written out (the pages' engine dequantizes PN weights for a chunked
+ * prefill GEMM, "What the fork adds").  Products on MFMA in fp32, each
+ * block's partial sum scaled by its d in fp32; within the tolerance above.
+ *   W : packed rows, 4-byte aligned; K an even number of blocks (a multiple
+ *       of 160 for pn3t, 128 for pn4t), else PN_EUNSUPPORTED
+ *   X : M rows of fp16, 16-byte aligned, ldx >= K and a multiple of 8
+ *   Y : M rows of fp32, 4-byte aligned, ldy >= N, overwritten
+ *   M : >= 1 (at most 8,388,480)
+ * Allocates nothing; enqueued on `stream`. */
+pn_status pn_gemm_prefill(pn_type t, const void *W, int64_t N, int64_t K,
+                          const uint16_t *X, int64_t ldx, int64_t M,
+                          float *Y, int64_t ldy, void *stream);
+
 /* Arithmetic of the small-batch kernels.  Both read the weights the same way
  * and agree within the tolerance above:
  *   PN_SMALLM_MFMA  decoded weights feed matrix-core products

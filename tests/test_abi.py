@@ -95,6 +95,30 @@ def test_group_host_checks():
     lib.pn_group_destroy(None)
 
 
+def test_prefill_host_checks():
+    lib = B.lib()
+    X16 = 0x10000  # 16-byte aligned, never dereferenced
+    ok = dict(t=0, W=FAKE, N=4, K=640, X=X16, ldx=640, M=3, Y=FAKE, ldy=4)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.pn_gemm_prefill(a["t"], a["W"], a["N"], a["K"], a["X"], a["ldx"], a["M"], a["Y"], a["ldy"], None)
+    assert call(t=7) == PN_EINVAL
+    assert call(W=None) == PN_EINVAL
+    assert call(X=None) == PN_EINVAL
+    assert call(Y=None) == PN_EINVAL
+    assert call(K=81) == PN_ESHAPE
+    assert call(M=0) == PN_ESHAPE
+    assert call(ldx=320) == PN_ESHAPE
+    assert call(ldy=3) == PN_ESHAPE
+    assert call(K=80 * 3, ldx=240) == -4  # an odd number of blocks
+    assert call(t=1, K=64 * 5, ldx=320) == -4
+    assert call(W=FAKE + 2) == PN_EALIGN
+    assert call(X=X16 + 8) == PN_EALIGN
+    assert call(ldx=644) == PN_EALIGN
+    assert call(Y=FAKE + 2) == PN_EALIGN
+
+
 def test_rotate_host_checks():
     lib = B.lib()
     assert lib.pn_rotate(None, 1024, 1, 1024, FAKE, 1024, None) == PN_EINVAL
