@@ -49,22 +49,29 @@ namespace {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kPfThreads = 256;  // four waves
-constexpr int kPfM = 128;        // X rows per workgroup
-constexpr int kPfN = 128;        // weight rows per workgroup
-constexpr int kPfPad = 8;        // fp16 of padding per X row in LDS
-constexpr int kPairDw = 17;      // dwords per block pair
+constexpr int kPfWaves = 8;
+constexpr int kPfThreads = 64 * kPfWaves;
+constexpr int kPfM = 128;    // X rows per workgroup (two waves' 64)
+constexpr int kPfN = 256;    // weight rows per workgroup (four waves' 64)
+constexpr int kPairDw = 17;  // dwords per block pair
 
 template <int TYPE>
 struct Pf {
     static constexpr int KS = TYPE == 0 ? 160 : 128;  // k per block pair
     static constexpr int BK = KS / 2;                 // k per block
     static constexpr int STEPS = BK / 16;             // MFMA k-steps per block
-    static constexpr int XROW = KS + kPfPad;          // fp16 per X row in LDS
-    static constexpr int XCH = KS / 8;                // 16-byte chunks per X row
-    static constexpr int XBYTES = kPfM * XROW * 2;
-    static constexpr int LDS = XBYTES + kPfN * kPairDw * 4;
+    static constexpr int XCH = KS / 8;                // 16-byte chunks of an X row per pair
+    static constexpr int XSL = XCH + 1;               // LDS slots per X row (one pad slot)
+    static constexpr int XDMA = kPfM * XSL / 64;      // X DMA instructions per stage
+    static constexpr int XBYTES = 1024 * XDMA;
+    static constexpr int WDMA = kPfN * kPairDw / 64;  // W DMA instructions (4 bytes a lane)
+    static constexpr int STAGE = XBYTES + 256 * WDMA;
+    static constexpr int XPER = (XDMA + kPfWaves - 1) / kPfWaves;  // X DMA instructions per wave (at most)
+    static constexpr int WPER = (WDMA + kPfWaves - 1) / kPfWaves;
+    static constexpr int LDS = 2 * STAGE;
+    static_assert(kPfM * XSL % 64 == 0 && kPfN * kPairDw % 64 == 0, "whole DMA instructions");
 };
 
 struct PfArgs {
@@ -73,6 +80,7 @@ struct PfArgs {
     float *Y;
     int64_t ldx, ldy;
     int32_t N, M, S, pairs;  // S: row bytes; pairs: block pairs per row
+    int32_t splits;          // K slices (grid z); > 1: Y is zeroed first and the slices add into it
 };
 
 __device__ __forceinline__ half8_t cat4(half2_t a, half2_t b, half2_t c, half2_t d)
@@ -81,8 +89,8 @@ __device__ __forceinline__ half8_t cat4(half2_t a, half2_t b, half2_t c, half2_t
                                    0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Word j of block b of a staged block pair (17 dwords from LDS at p): the
-// first block's words are two bytes off the dword grid.
+// Word j of block b of a staged block pair (17 dwords at p): the first
+// block's words are two bytes off the dword grid.
 __device__ __forceinline__ uint32_t pair_word(const uint32_t *p, int b, int j)
 {
     return b == 0 ? __builtin_amdgcn_alignbit(p[j + 1], p[j], 16) : p[9 + j];
@@ -93,18 +101,73 @@ __device__ __forceinline__ float pair_scale(const uint32_t *p, int b)
     return half_bits_to_float(b == 0 ? p[0] & 0xffffu : p[8] >> 16);
 }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, (int)bytes, 0x00020000);
+}
+
+// Stage one block pair: X rows m0 .. m0+127 (k of the pair; rows past M read
+// zeros), 16 bytes a lane with one pad slot per row, and the block pairs of
+// weight rows n0 .. n0+255 (rows past N read zeros), 4 bytes a lane.  The
+// instructions are dealt to the waves round-robin; a lane's offsets within
+// the tiles are the same for every pair (pf_offsets) and the pair moves the
+// scalar offset only.
+template <int TYPE>
+__device__ __forceinline__ void pf_offsets(uint32_t (&xo)[Pf<TYPE>::XPER], uint32_t (&wo)[Pf<TYPE>::WPER],
+                                           uint32_t xrow, uint32_t wrow, int wave, int lane)
+{
+    using C = Pf<TYPE>;
+#pragma unroll
+    for (int t = 0; t < C::XPER; ++t) {
+        const uint32_t q = 64u * (uint32_t)(wave + kPfWaves * t) + (uint32_t)lane;
+        const uint32_t r = q / C::XSL, ch = q - r * C::XSL;
+        xo[t] = ch < (uint32_t)C::XCH ? r * xrow + 16u * ch : 0x80000000u;
+    }
+#pragma unroll
+    for (int t = 0; t < C::WPER; ++t) {
+        const uint32_t q = 64u * (uint32_t)(wave + kPfWaves * t) + (uint32_t)lane;
+        const uint32_t r = q / kPairDw, d = q - r * kPairDw;
+        wo[t] = r * wrow + 4u * d;
+    }
+}
+
+template <int TYPE>
+__device__ __forceinline__ void stage_pair(uint8_t *st, const __amdgpu_buffer_rsrc_t &xr, const __amdgpu_buffer_rsrc_t &wr,
+                                           const uint32_t (&xo)[Pf<TYPE>::XPER], const uint32_t (&wo)[Pf<TYPE>::WPER],
+                                           int p, int wave)
+{
+    using C = Pf<TYPE>;
+    const int xso = p * C::KS * 2, wso = p * 68;
+#pragma unroll
+    for (int t = 0; t < C::XPER; ++t) {
+        const int i = wave + kPfWaves * t;
+        if (i < C::XDMA)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)(st + 1024 * i), 16, (int)xo[t], xso, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < C::WPER; ++t) {
+        const int i = wave + kPfWaves * t;
+        if (i < C::WDMA)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void *)(st + C::XBYTES + 256 * i), 4, (int)wo[t], wso, 0,
+                                                     0);
+    }
+}
+
 template <int TYPE>
 __global__ __launch_bounds__(kPfThreads) void gemm_prefill(PfArgs a)
 {
     using C = Pf<TYPE>;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    uint16_t *xs = (uint16_t *)lds;
-    uint32_t *ws = (uint32_t *)(lds + C::XBYTES);
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave & 1, wn = wave >> 1;
     const int h = lane >> 5, c = lane & 31;
     const int n0 = blockIdx.x * kPfN, m0 = blockIdx.y * kPfM;
+    const int xrows = a.M - m0 < kPfM ? a.M - m0 : kPfM;
+    const int wrows = a.N - n0 < kPfN ? a.N - n0 : kPfN;
+    const uint32_t xrow = (uint32_t)a.ldx * 2u, wrow = (uint32_t)a.S;
+    const __amdgpu_buffer_rsrc_t xr = rsrc(a.X + (int64_t)m0 * a.ldx, (uint32_t)xrows * xrow);
+    const __amdgpu_buffer_rsrc_t wr = rsrc(a.W + (int64_t)n0 * a.S, (uint32_t)wrows * wrow);
 
     float16_t acc[2][2];
 #pragma unroll
@@ -112,23 +175,21 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill(PfArgs a)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = (float16_t){};
 
-    for (int p = 0; p < a.pairs; ++p) {
-        __syncthreads();  // the previous pair's reads are done
-        for (int i = threadIdx.x; i < kPfM * C::XCH; i += kPfThreads) {
-            const int r = i / C::XCH, ch = i - r * C::XCH;
-            const int m = m0 + r;
-            u32x4 v = (u32x4){0u, 0u, 0u, 0u};
-            if (m < a.M) v = *(const u32x4 *)(a.X + (int64_t)m * a.ldx + (int64_t)p * C::KS + 8 * ch);
-            *(u32x4 *)(xs + r * C::XROW + 8 * ch) = v;
-        }
-        for (int i = threadIdx.x; i < kPfN * kPairDw; i += kPfThreads) {
-            const int r = i / kPairDw, d = i - r * kPairDw;
-            const int n = n0 + r;
-            uint32_t v = 0u;
-            if (n < a.N) v = *(const uint32_t *)(a.W + (int64_t)n * a.S + 68 * (int64_t)p + 4 * d);
-            ws[r * kPairDw + d] = v;
-        }
+    // this workgroup's slice of the block pairs
+    const int p0 = (int)((int64_t)a.pairs * blockIdx.z / a.splits);
+    const int p1 = (int)((int64_t)a.pairs * (blockIdx.z + 1) / a.splits);
+    uint32_t xo[C::XPER], wo[C::WPER];
+    pf_offsets<TYPE>(xo, wo, xrow, wrow, wave, lane);
+    stage_pair<TYPE>(lds, xr, wr, xo, wo, p0, wave);
+    for (int p = p0; p < p1; ++p) {
+        // this wave's loads of pair p have landed; after the barrier, every
+        // wave's have, and every wave is done with pair p - 1's stage
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
         __syncthreads();
+        uint8_t *st = lds + ((p - p0) & 1) * C::STAGE;
+        if (p + 1 < p1) stage_pair<TYPE>(lds + ((p - p0 + 1) & 1) * C::STAGE, xr, wr, xo, wo, p + 1, wave);
+        const uint16_t *xs = (const uint16_t *)st;
+        const uint32_t *ws = (const uint32_t *)(st + C::XBYTES);
 
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
@@ -160,7 +221,7 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill(PfArgs a)
                 }
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt) {
-                    const uint16_t *px = xs + (wm * 64 + mt * 32 + c) * C::XROW;
+                    const uint16_t *px = xs + (wm * 64 + mt * 32 + c) * (8 * C::XSL);
                     half8_t A;
                     if constexpr (TYPE == 0) {
                         const int k = 80 * b + 40 * h + 2 * s;
@@ -192,9 +253,23 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill(PfArgs a)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int m = m0 + wm * 64 + mt * 32 + 8 * (v / 4) + 4 * h + (v % 4);
-                if (m < a.M && n < a.N) a.Y[(int64_t)m * a.ldy + n] = acc[mt][nt][v];
+                if (m < a.M && n < a.N) {
+                    float *y = a.Y + (int64_t)m * a.ldy + n;
+                    if (a.splits > 1)
+                        __hip_atomic_fetch_add(y, acc[mt][nt][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    else
+                        *y = acc[mt][nt][v];
+                }
             }
         }
+}
+
+// Y[m][0..N) = 0 for m < M, ahead of a split launch (a kernel rather than a
+// memset, so that the call can be captured into a graph).
+__global__ __launch_bounds__(256) void zero_rows(float *Y, int64_t ldy, int32_t N, int32_t M)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < (int64_t)N * M) Y[(i / N) * ldy + i % N] = 0.0f;
 }
 
 bool set_prefill_attr()
@@ -224,6 +299,8 @@ pn_status pn_gemm_prefill(pn_type t, const void *W, int64_t N, int64_t K, const 
     if (nb % 2 != 0) return PN_EUNSUPPORTED;  // whole block pairs only
     if (((uintptr_t)W & 3) || ((uintptr_t)X & 15) || (ldx & 7) || !aligned4(Y)) return PN_EALIGN;
     if (M > INT32_MAX - kPfM || (M + kPfM - 1) / kPfM > 65535) return PN_EUNSUPPORTED;
+    if ((uint64_t)kPfM * (uint64_t)ldx * 2u >= 0x80000000ull) return PN_EUNSUPPORTED;  // 32-bit tile offsets
+    if (N * M > ((int64_t)1 << 40)) return PN_EUNSUPPORTED;
     if (!set_prefill_attr()) return PN_ELAUNCH;
     PfArgs a;
     a.W = (const uint8_t *)W;
@@ -235,8 +312,21 @@ pn_status pn_gemm_prefill(pn_type t, const void *W, int64_t N, int64_t K, const 
     a.M = (int32_t)M;
     a.S = (int32_t)(nb * 34);
     a.pairs = (int32_t)(nb / 2);
-    const dim3 grid((unsigned)((N + kPfN - 1) / kPfN), (unsigned)((M + kPfM - 1) / kPfM));
+    // One workgroup per CU (the two LDS stages take 102-118 KiB).  When the
+    // output tiles cannot fill the CUs, split K into as many slices as keep
+    // one round of workgroups, each slice at least 4 block pairs.
+    const int64_t tiles = ((N + kPfN - 1) / kPfN) * ((M + kPfM - 1) / kPfM);
+    int64_t splits = tiles >= device_cus() ? 1 : device_cus() / tiles;
+    if (splits > a.pairs / 4) splits = a.pairs / 4;
+    if (splits < 1) splits = 1;
+    a.splits = (int32_t)splits;
+    const dim3 grid((unsigned)((N + kPfN - 1) / kPfN), (unsigned)((M + kPfM - 1) / kPfM), (unsigned)splits);
     const hipStream_t s = (hipStream_t)stream;
+    if (splits > 1) {
+        const int64_t n = N * M;
+        hipLaunchKernelGGL(zero_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, Y, ldy, (int32_t)N, (int32_t)M);
+        if (hipGetLastError() != hipSuccess) return PN_ELAUNCH;
+    }
     if (t == PN_PN3T)
         hipLaunchKernelGGL(gemm_prefill<0>, grid, dim3(kPfThreads), Pf<0>::LDS, s, a);
     else
