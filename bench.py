@@ -123,6 +123,51 @@ def per_config_timing(B, synth, torch):
     return out
 
 
+PEAK_TFLOPS_F16 = 2500.0  # MI355X dense fp16 MFMA, AMD's published figure
+
+
+def prefill_timing(B, synth, torch, m=512):
+    """Prefill of one 27B-shaped decoder layer (q, k, v, o, gate, up, down;
+    pn_gemm_prefill, weights decoded inside the MFMA GEMM) for an m-token
+    prompt chunk: HIP events around each product, median of 10 after 3
+    warm-up calls.  Flops = 2 m N K per product."""
+    import numpy as np
+    dev = torch.device("cuda")
+    g = synth.rng(5, 0, 0)
+    per = {}
+    total_ms = 0.0
+    flops = 0
+    for name, t, n, k in synth.SWEEP_LAYER:
+        w = torch.from_numpy(synth.random_blocks(g, t, n, k)).to(dev)
+        x = torch.from_numpy(synth.activation(g, k, m)).to(dev)
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        run = lambda: B.pn_gemm_prefill(t, w, n, k, x, k, m, y, n)
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        for a, b in ev:
+            a.record()
+            run()
+            b.record()
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+        f = 2 * m * n * k
+        per[name] = {"ms": round(ms, 4), "tflops": round(f / (ms * 1e-3) / 1e12, 1)}
+        total_ms += ms
+        flops += f
+        del w, x, y
+    torch.cuda.empty_cache()
+    tf = flops / (total_ms * 1e-3) / 1e12
+    return {"workload": "prefill of one 27B-shaped layer, %d-token chunk" % m, "tokens": m,
+            "ms_per_layer": round(total_ms, 4), "tflops": round(tf, 1),
+            "tokens_per_s_64_layers": round(m / (64 * total_ms * 1e-3), 1),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_TFLOPS_F16, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_TFLOPS_F16, 4), "traffic": None,
+                         "kernel": "gemm_prefill", "note": "sum over the layer's seven products"},
+            "per_matrix": per}
+
+
 def host_read_gbps():
     """Host memory read rate (numpy sum over 1 GiB of uint64, best of 3)."""
     import numpy as np
@@ -331,6 +376,10 @@ def main():
     if not args.no_configs and m is None:
         log("one-call timings of workloads 0-2")
         per_config = per_config_timing(B, synth, torch)
+    prefill = None
+    if not args.no_secondary and m is None:
+        log("prefill of one layer, 512-token chunk")
+        prefill = prefill_timing(B, synth, torch)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -377,6 +426,7 @@ def main():
         "cpu_baseline": cpu,
         "other_schedules": secondary,
         "per_config": per_config,
+        "prefill": prefill,
         "kernel_hash": kernel_hash(kind),
     }
     print(json.dumps(out), flush=True)
