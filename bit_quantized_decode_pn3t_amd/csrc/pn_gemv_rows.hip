@@ -26,15 +26,17 @@
 //
 // Loads.  A stage is one window of the tile: 16 rows x 1088 bytes, brought
 // to LDS by 16-byte DMA instructions (buffer_load_dwordx4 ... lds), rows
-// 1104 bytes apart in LDS so that the lanes' period reads do not collide in
-// banks.  Each wave has one stage: once its lanes have read their periods
+// 976 bytes apart in LDS so that the lanes' period reads do not collide in
+// banks; the last 8 chunks of each row go to a separate region with the
+// normal cache policy (the 128-byte line they share with the next window
+// then is often still cached when that window is fetched).  Each wave has one stage: once its lanes have read their periods
 // into registers, the stage is refilled with the wave's next window, in two
 // pieces between the block pairs' products, so that the next window is in
 // flight while this one is computed.  x for a stage comes from global
 // memory (L2) into registers, five dwordx4 per lane.
 //
 // Grid.  One workgroup of eight waves per CU (two per SIMD: one computes
-// while the other waits; the stages take 144 KiB of LDS).  Inline launches
+// while the other waits; the stages take 152 KiB of LDS).  Inline launches
 // (one matrix, or the fused pair) split their tiles evenly over the waves;
 // group launches (many matrices, one launch) hand tiles out from pools of
 // per-pool atomic counters, longest tiles first.  A launch with few tiles
@@ -65,6 +67,11 @@ namespace {
 //   PN_ROWS_STAGES ring stages per wave: 2 (4 waves per CU, one per SIMD,
 //                  two windows in flight per wave) or 1 (8 waves per CU,
 //                  two per SIMD: one computes while the other waits);
+//   PN_ROWS_BND    each row's last 8 chunks of a window (where a 128-byte
+//                  line shared with the next window lies) in an LDS region
+//                  of their own, filled by 3 DMA instructions with the
+//                  normal cache policy, the rest nontemporal: fetched bytes
+//                  1.073 -> 1.051 of the algorithmic ones, ~1 % faster;
 //   PN_ROWS_SPREAD pieces a stage's DMA is issued in, between the block
 //                  pairs' products (1: all at once, which stalls the wave
 //                  while the eight waves' bursts queue up; 2 or 3).
@@ -80,6 +87,9 @@ namespace {
 #ifndef PN_ROWS_STAGES
 #define PN_ROWS_STAGES 1
 #endif
+#ifndef PN_ROWS_BND
+#define PN_ROWS_BND 1
+#endif
 #ifndef PN_ROWS_SPREAD
 #define PN_ROWS_SPREAD 2
 #endif
@@ -92,11 +102,19 @@ constexpr int kPeriod = 272;                  // 8 blocks
 constexpr int kWindow = 4 * kPeriod;          // tile-row bytes per stage
 constexpr int kRowLds = PN_ROWS_PAD ? kWindow + 16 : kWindow;  // LDS bytes per tile row
 constexpr int kRowSlots = kRowLds / 16;      // 16-byte DMA slots per tile row
-constexpr int kDma = (kTileRows * kRowSlots + 63) / 64;  // DMA instructions per stage
+// PN_ROWS_BND: the last 8 chunks of each row's window (where a line shared
+// with the next window lies) go to a region of their own, filled with the
+// normal cache policy so that the next window finds the line cached.
+constexpr int kMainCk = PN_ROWS_BND ? 60 : 68;  // chunks per row in the main region
+constexpr int kMainSlots = PN_ROWS_BND ? 61 : kRowSlots;
+constexpr int kMainDma = (kTileRows * kMainSlots + 63) / 64;
+constexpr int kBndSlots = 9;                    // boundary region: 8 chunks + pad per row
+constexpr int kBndDma = PN_ROWS_BND ? (kTileRows * kBndSlots + 63) / 64 : 0;
+constexpr int kDma = kMainDma + kBndDma;        // DMA instructions per stage
 constexpr int kStage = 1024 * kDma;          // LDS bytes per stage
 constexpr int kXLoads = 5;                    // x loads per lane per stage
 constexpr int kLater = (kNS - 1) * (kDma + kXLoads);  // VMEM instructions issued after a stage
-constexpr int kRing = kRWaves * kNS * kStage;  // 147,456 (139,264 unpadded) bytes of LDS
+constexpr int kRing = kRWaves * kNS * kStage;  // 155,648 bytes of LDS (147,456 without the boundary region)
 constexpr int kMinTilesPerCu = 32;            // below this "auto" uses gemv_stream
 constexpr int kPools = 16;                    // tile pools of a group launch
 constexpr int kCounterStride = 1024;          // uint32s between pool counters (4 KiB)
@@ -179,6 +197,19 @@ __device__ __forceinline__ void load_period(const uint8_t *src, uint32_t (&D)[68
 #pragma unroll
     for (int t = 0; t < 17; ++t) {
         const u32x4 v = *(const u32x4 *)(src + 16 * t);
+        D[4 * t] = v[0];
+        D[4 * t + 1] = v[1];
+        D[4 * t + 2] = v[2];
+        D[4 * t + 3] = v[3];
+    }
+}
+
+// The same, with chunks 9..16 from a second base (the boundary region).
+__device__ __forceinline__ void load_period2(const uint8_t *lo, const uint8_t *hi, uint32_t (&D)[68])
+{
+#pragma unroll
+    for (int t = 0; t < 17; ++t) {
+        const u32x4 v = *(const u32x4 *)((t < 9 ? lo : hi) + 16 * t);
         D[4 * t] = v[0];
         D[4 * t + 1] = v[1];
         D[4 * t + 2] = v[2];
@@ -372,17 +403,31 @@ struct Slot {
     int32_t nrows;  // rows of the tile that exist
 };
 
-// Per-lane DMA offsets for row stride S: slot q = 64 i + lane holds chunk
-// q % kRowSlots of tile row q / kRowSlots; pad slots and slots past the
-// last row get an out-of-range offset (they read nothing).
+// The chunk (0..67) of a tile row that slot 64 i + lane of a stage holds,
+// or 68 for a pad slot or one past the last row.
+__device__ __forceinline__ uint32_t slot_chunk(int i, int lane, uint32_t &row)
+{
+    if (i < kMainDma) {
+        const uint32_t q = 64u * i + (uint32_t)lane;
+        row = q / (uint32_t)kMainSlots;
+        const uint32_t ck = q - (uint32_t)kMainSlots * row;
+        return row < (uint32_t)kTileRows && ck < (uint32_t)kMainCk ? ck : 68u;
+    }
+    const uint32_t q = 64u * (i - kMainDma) + (uint32_t)lane;
+    row = q / (uint32_t)kBndSlots;
+    const uint32_t cc = q - (uint32_t)kBndSlots * row;
+    return row < (uint32_t)kTileRows && cc < 8u ? (uint32_t)kMainCk + cc : 68u;
+}
+
+// Per-lane DMA offsets for row stride S (see slot_chunk); pad slots and
+// slots past the last row get an out-of-range offset (they read nothing).
 __device__ __forceinline__ void dma_offsets(uint32_t (&vo)[kDma], int32_t S, int lane)
 {
 #pragma unroll
     for (int i = 0; i < kDma; ++i) {
-        const uint32_t q = 64u * i + (uint32_t)lane;
-        const uint32_t row = q / (uint32_t)kRowSlots;
-        const uint32_t ck = q - (uint32_t)kRowSlots * row;
-        vo[i] = row < (uint32_t)kTileRows && ck < 68u ? row * (uint32_t)S + 16u * ck : 0x80000000u;
+        uint32_t row;
+        const uint32_t ck = slot_chunk(i, lane, row);
+        vo[i] = ck < 68u ? row * (uint32_t)S + 16u * ck : 0x80000000u;
     }
 }
 
@@ -418,12 +463,20 @@ template <int I0, int I1>
 __device__ __forceinline__ void dma_part(const Dma &d, uint8_t *stage, const uint32_t (&vo)[kDma], int lane)
 {
 #pragma unroll
-    for (int i = I0; i < I1; ++i) {
-        const uint32_t q = 64u * i + (uint32_t)lane;
-        const uint32_t ck = q - (uint32_t)kRowSlots * (q / (uint32_t)kRowSlots);
+    for (int i = I0; i < (I1 < kMainDma ? I1 : kMainDma); ++i) {
+        uint32_t row;
+        const uint32_t ck = slot_chunk(i, lane, row);
         const uint32_t off = ck < d.nck ? vo[i] : 0x80000000u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(d.wr, (lds_void *)(stage + 1024 * i), 16, (int)off, (int)d.soff, 0,
                                                  2 /* nontemporal */);
+    }
+#pragma unroll
+    for (int i = (I0 > kMainDma ? I0 : kMainDma); i < I1; ++i) {
+        uint32_t row;
+        const uint32_t ck = slot_chunk(i, lane, row);
+        const uint32_t off = ck < d.nck ? vo[i] : 0x80000000u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.wr, (lds_void *)(stage + 1024 * i), 16, (int)off, (int)d.soff, 0,
+                                                 0 /* normal: kept for the next window */);
     }
 }
 
@@ -550,7 +603,13 @@ __global__ __launch_bounds__(kRThreads) void gemv_rows(RArgs a)
             // use of D wait for all 17 reads.
             wait_lds_reads();
             uint32_t D[68];
-            load_period(stage + r * kRowLds + g * kPeriod, D);
+            if constexpr (PN_ROWS_BND) {
+                const uint8_t *lo = stage + 16 * (kMainSlots * r + 17 * g);
+                const uint8_t *hi = g == 3 ? stage + 1024 * kMainDma + 16 * (kBndSlots * r - 9) : lo;
+                load_period2(lo, hi, D);
+            } else {
+                load_period(stage + r * kRowLds + g * kPeriod, D);
+            }
             if (pend) *pend_a = pend_v;
             pend = 0;
             float it = 0.0f;
