@@ -31,9 +31,10 @@
 //         takes word 2s + h in lane half h, and X at 64 b + 16 s + 8 h + e.
 //   pn3t  a word holds 10 codes, which do not fall on the 8-code grid; the
 //         k order inside a block is permuted instead (a GEMM's sum is
-//         order-free if A and B agree): lane half h takes words 4h .. 4h+3,
-//         and k-step s takes code pair s of each of them; X is read at the
-//         same permuted positions 80 b + 40 h + 10 j + 2 s + {0, 1}.
+//         order-free if A and B agree): lane half h owns codes 40h .. 40h+39
+//         (its words 4h .. 4h+3) and k-step s takes codes 40h + 8s .. +7,
+//         the lane's code pairs 4s .. 4s+3; X is read at 80 b + 40 h + 8 s,
+//         one aligned 16-byte read like pn4t's.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -214,23 +215,17 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill(PfArgs a)
                 half8_t B[2];
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
-                    if constexpr (TYPE == 0)
-                        B[nt] = cat4(u[nt][0][s], u[nt][1][s], u[nt][2][s], u[nt][3][s]);
+                    if constexpr (TYPE == 0)  // the lane's code pairs 4s .. 4s+3 (pair i: word i / 5, pair i % 5)
+                        B[nt] = cat4(u[nt][(4 * s) / 5][(4 * s) % 5], u[nt][(4 * s + 1) / 5][(4 * s + 1) % 5],
+                                     u[nt][(4 * s + 2) / 5][(4 * s + 2) % 5], u[nt][(4 * s + 3) / 5][(4 * s + 3) % 5]);
                     else
                         B[nt] = cat4(u[nt][s][0], u[nt][s][1], u[nt][s][2], u[nt][s][3]);
                 }
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt) {
                     const uint16_t *px = xs + (wm * 64 + mt * 32 + c) * (8 * C::XSL);
-                    half8_t A;
-                    if constexpr (TYPE == 0) {
-                        const int k = 80 * b + 40 * h + 2 * s;
-                        A = cat4(as_half2(*(const uint32_t *)(px + k)), as_half2(*(const uint32_t *)(px + k + 10)),
-                                 as_half2(*(const uint32_t *)(px + k + 20)),
-                                 as_half2(*(const uint32_t *)(px + k + 30)));
-                    } else {
-                        A = __builtin_bit_cast(half8_t, *(const u32x4 *)(px + 64 * b + 16 * s + 8 * h));
-                    }
+                    const int k = TYPE == 0 ? 80 * b + 40 * h + 8 * s : 64 * b + 16 * s + 8 * h;
+                    const half8_t A = __builtin_bit_cast(half8_t, *(const u32x4 *)(px + k));
 #pragma unroll
                     for (int nt = 0; nt < 2; ++nt)
                         P[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B[nt], P[mt][nt], 0, 0, 0);
