@@ -1,0 +1,75 @@
+"""The new entry points under HIP graph capture: a split-K prefill product
+(its zero fill is a kernel, so the call can be captured) and a plan with
+rotated inputs (its rotation launch is replayed with the GEMV launch).  Each
+graph is replayed several times, with eager work and synchronizations
+between the replays, and every replay is checked against the oracle."""
+import numpy as np
+import pytest
+
+from gpu_util import assert_gemv_close, dev, say, sync
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+from bit_quantized_decode_pn3t_amd import _binding as B  # noqa: E402
+from bit_quantized_decode_pn3t_amd import synth  # noqa: E402
+from oracle import pnref  # noqa: E402
+
+
+def test_prefill_split_k_graph_replays():
+    t, n, k, m = "pn4t", 1024, 5120, 96  # four output tiles: the launch splits K
+    g = np.random.default_rng(31)
+    w = synth.random_blocks(g, t, n, k)
+    xm = synth.activation(g, k, m)
+    y64, a = pnref.gemm_f64(t, w, n, k, xm)
+    wd = dev(w.reshape(-1))
+    xd = dev(xm)
+    y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    say("prefill graph: eager")
+    B.pn_gemm_prefill(t, wd, n, k, xd, k, m, y, n)
+    sync()
+    assert_gemv_close(y.cpu().numpy(), y64, a, "prefill eager")
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        B.pn_gemm_prefill(t, wd, n, k, xd, k, m, y, n)
+    sync()
+    for rep in range(3):
+        say("prefill graph: replay %d" % rep)
+        y.fill_(float("nan"))  # eager work between the replays
+        sync()
+        gr.replay()
+        sync()
+        assert_gemv_close(y.cpu().numpy(), y64, a, "prefill replay %d" % rep)
+
+
+def test_rotated_plan_graph_replays():
+    specs = [("pn3t", 64, 5120), ("pn4t", 48, 6144), ("pn4t", 32, 17408)]
+    host, probs = [], []
+    for i, (t, n, k) in enumerate(specs):
+        g = np.random.default_rng([41, i])
+        w = synth.random_blocks(g, t, n, k)
+        host.append((t, w, n, k, g))
+        probs.append((t, dev(w.reshape(-1)), n, k, dev(synth.activation(g, k)),
+                      torch.empty(n, dtype=torch.float32, device="cuda")))
+    plan = B.Group(probs, rotate=True)
+    plan.run()  # warm
+    sync()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        plan.run()
+    sync()
+    for rep in range(3):
+        # new activations each time: the replayed rotation must see them
+        for (t, w, n, k, g), p in zip(host, probs):
+            p[4].copy_(dev(synth.activation(g, k)))
+            p[5].fill_(float("nan"))
+        sync()
+        say("rotated plan graph: replay %d" % rep)
+        gr.replay()
+        sync()
+        for (t, w, n, k, g), p in zip(host, probs):
+            x = p[4].cpu().numpy()
+            y64, a = pnref.gemv_f64(t, w, n, k, pnref.rotate(x))
+            assert_gemv_close(p[5].cpu().numpy(), y64, a, "rotated plan replay %d %s" % (rep, t))
+    plan.close()
