@@ -54,8 +54,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kPfWaves = 8;
 constexpr int kPfThreads = 64 * kPfWaves;
-constexpr int kPfM = 128;    // X rows per workgroup (two waves' 64)
-constexpr int kPfN = 256;    // weight rows per workgroup (four waves' 64)
+constexpr int kPfM = 128;    // X rows per workgroup
+constexpr int kPfN = 256;    // weight rows per workgroup
 constexpr int kPairDw = 17;  // dwords per block pair
 // 32-row X tiles per wave: 4 (each wave decodes its own 32 weight rows and
 // multiplies them by all 128 X rows) or 2 (2 x 2 tiles: two waves decode the
