@@ -274,8 +274,9 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill(PfArgs a)
 // memset, so that the call can be captured into a graph).
 __global__ __launch_bounds__(256) void zero_rows(float *Y, int64_t ldy, int32_t N, int32_t M)
 {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < (int64_t)N * M) Y[(i / N) * ldy + i % N] = 0.0f;
+    const int64_t n = (int64_t)N * M;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        Y[(i / N) * ldy + i % N] = 0.0f;
 }
 
 bool set_prefill_attr()
@@ -330,7 +331,8 @@ pn_status pn_gemm_prefill(pn_type t, const void *W, int64_t N, int64_t K, const 
     const hipStream_t s = (hipStream_t)stream;
     if (splits > 1) {
         const int64_t n = N * M;
-        hipLaunchKernelGGL(zero_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, Y, ldy, (int32_t)N, (int32_t)M);
+        const int64_t blocks = (n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536;
+        hipLaunchKernelGGL(zero_rows, dim3((unsigned)blocks), dim3(256), 0, s, Y, ldy, (int32_t)N, (int32_t)M);
         if (hipGetLastError() != hipSuccess) return PN_ELAUNCH;
     }
     if (t == PN_PN3T)
