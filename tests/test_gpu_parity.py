@@ -343,10 +343,12 @@ def test_group(gemv_kernel, which):
 # ---------------------------------------------------------------------------
 MATHS = ["mfma", "valu"]
 # (type, N, K): several 32-row wave tiles with ragged tails, rows shorter than
-# the 2U-block pipeline (1 and 7 blocks), and activations that take several
-# LDS chunks at M = 8 (pn3t K = 5120: 2 chunks; pn4t K = 17408: 5 chunks).
+# the 2U-block pipeline (1 and 7 blocks), rows for the in-order U-slot
+# pipeline (9 and 11 blocks: at least 2U, fewer than the grouped pipeline's
+# 4U), and activations that take several LDS chunks at M = 8 (pn3t K = 5120:
+# 2 chunks; pn4t K = 17408: 5 chunks).
 SMALLM_SHAPES = [("pn3t", 256, 5120), ("pn4t", 300, 17408), ("pn4t", 33, 6144), ("pn3t", 7, 80),
-                 ("pn4t", 19, 64 * 9), ("pn3t", 45, 80 * 7), ("pn4t", 1000, 5120)]
+                 ("pn4t", 19, 64 * 9), ("pn3t", 45, 80 * 7), ("pn3t", 40, 80 * 11), ("pn4t", 1000, 5120)]
 
 
 @pytest.fixture
