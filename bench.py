@@ -337,7 +337,7 @@ def main():
         achieved = bytes_per_token / (kern_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / PEAK_GBPS, 4), "traffic": measured_traffic(workload, kind),
-                    "kernel": variant.replace("_group", "") if m is None else "gemm_stream<%s>" % args.math,
+                    "kernel": variant.replace("_group", ""),
                     "variant": variant, "kernel_avg_ms": round(kern_ms, 4),
                     "kernel_ms_min_p50_max": [round(min(ev_ms), 4), round(sorted(ev_ms)[len(ev_ms) // 2], 4),
                                               round(max(ev_ms), 4)],

@@ -189,7 +189,9 @@ def pn_get_smallm_math():
 
 def pn_set_gemv_kernel(kernel, check=True):
     """Select the M = 1 kernel: "auto" (row tiles for large launches),
-    "stream" (register pipeline) or "rows" (row tiles wherever they apply)."""
+    "stream" (register pipeline) or "rows" (row tiles wherever they apply).
+    "stream" also keeps the small-M MFMA products on register loads; otherwise
+    those whose rows are whole periods are staged through LDS by DMA."""
     st = lib().pn_set_gemv_kernel(GEMV_KERNEL.get(kernel, kernel if isinstance(kernel, int) else -1))
     if check:
         _check(st, "pn_set_gemv_kernel")

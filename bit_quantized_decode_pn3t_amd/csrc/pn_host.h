@@ -26,6 +26,8 @@ enum Variant {
     kVarGroupRows = 10,
     kVarRotate = 11,
     kVarPrefill = 12,
+    kVarSmallMRows = 13,
+    kVarGroupSmallMRows = 14,
 };
 
 extern thread_local int g_last_variant;

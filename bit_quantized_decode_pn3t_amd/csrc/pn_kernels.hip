@@ -808,6 +808,8 @@ const char *pn_variant_name(int v)
     case kVarSmallMMfma: return "gemm_stream_mfma";
     case kVarGroupSmallMValu: return "gemm_stream_valu_group";
     case kVarGroupSmallMMfma: return "gemm_stream_mfma_group";
+    case kVarSmallMRows: return "gemm_rows_mfma";
+    case kVarGroupSmallMRows: return "gemm_rows_mfma_group";
     case kVarRows: return "gemv_rows";
     case kVarGroupRows: return "gemv_rows_group";
     case kVarRotate: return "hadamard_rotate";

@@ -36,6 +36,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "pn_device.h"
 #include "pn_host.h"
 
@@ -76,6 +78,7 @@ constexpr int kTileRows = kSmWaves * kWaveRows;
 constexpr int kSmLdsMax = PN_SM_LDS_KB * 1024;
 constexpr int kSmLdsValu = PN_SM_VALU_LDS_KB * 1024;
 constexpr int kMaxM = 16;  // the MFMA tile has 16 activation rows
+constexpr int kSmFlagDma = 0x10;  // group plan flag: run by gemm_rows
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -436,6 +439,29 @@ __device__ __forceinline__ int sm_tile0(const SmArgs &a, int i)
     return a.table ? a.table[i].tile0 : a.p0.tile0;
 }
 
+// The problem of `tile` (the tiles of a launch go through the problems in
+// order): advance i to it and load its record, wave-uniform.
+__device__ __forceinline__ void sm_next_problem(const SmArgs &args, int tile, int &i, int &next0, SmProb &p)
+{
+    if (next0 >= 0) ++i;
+    while (sm_tile0(args, i + 1) <= tile) ++i;
+    const SmProb &c = *sm_problem(args, i);
+    p.W = uniform_ptr(c.W);
+    p.X = uniform_ptr(c.X);
+    p.Y = uniform_ptr(c.Y);
+    p.ldx = ((int64_t)uniform((int32_t)(c.ldx >> 32)) << 32) | (uint32_t)uniform((int32_t)c.ldx);
+    p.ldy = ((int64_t)uniform((int32_t)(c.ldy >> 32)) << 32) | (uint32_t)uniform((int32_t)c.ldy);
+    p.N = uniform(c.N);
+    p.nb = uniform(c.nb);
+    p.M = uniform(c.M);
+    p.type = uniform(c.type);
+    p.tile0 = uniform(c.tile0);
+    p.cb = uniform(c.cb);
+    p.nchunks = uniform(c.nchunks);
+    p.stride = uniform(c.stride);
+    next0 = uniform(sm_tile0(args, i + 1));
+}
+
 // Workgroups take tiles (kSmWaves x 32 rows of one problem) in a grid
 // stride.  The activation chunk is restaged when the problem changes, and at
 // every chunk boundary of problems whose activations do not fit at once.
@@ -447,25 +473,7 @@ __global__ __launch_bounds__(kSmThreads) void gemm_stream(SmArgs args)
     int i = 0, next0 = -1, staged = -1;
     SmProb p;
     for (int tile = blockIdx.x; tile < args.total_tiles; tile += gridDim.x) {
-        if (tile >= next0) {
-            if (next0 >= 0) ++i;
-            while (sm_tile0(args, i + 1) <= tile) ++i;
-            const SmProb &c = *sm_problem(args, i);
-            p.W = uniform_ptr(c.W);
-            p.X = uniform_ptr(c.X);
-            p.Y = uniform_ptr(c.Y);
-            p.ldx = ((int64_t)uniform((int32_t)(c.ldx >> 32)) << 32) | (uint32_t)uniform((int32_t)c.ldx);
-            p.ldy = ((int64_t)uniform((int32_t)(c.ldy >> 32)) << 32) | (uint32_t)uniform((int32_t)c.ldy);
-            p.N = uniform(c.N);
-            p.nb = uniform(c.nb);
-            p.M = uniform(c.M);
-            p.type = uniform(c.type);
-            p.tile0 = uniform(c.tile0);
-            p.cb = uniform(c.cb);
-            p.nchunks = uniform(c.nchunks);
-            p.stride = uniform(c.stride);
-            next0 = uniform(sm_tile0(args, i + 1));
-        }
+        if (tile >= next0) sm_next_problem(args, tile, i, next0, p);
         if (p.nchunks > 1 || staged != i) {
             const int nbc = p.nb < p.cb ? p.nb : p.cb;
             __syncthreads();
@@ -481,6 +489,223 @@ __global__ __launch_bounds__(kSmThreads) void gemm_stream(SmArgs args)
             sm_tile<0, MFMA>(p, row0, lds);
         else
             sm_tile<1, MFMA>(p, row0, lds);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// gemm_rows: the MFMA product with the weights brought to LDS by DMA.
+//
+// gemm_stream's loads (a dwordx2 per lane, the four lanes of a quad on 32
+// bytes of one row, sixteen rows per instruction) cap that kernel near 4 TB/s
+// even with its arithmetic taken out: each request carries 32 bytes and
+// every 128-byte line is requested four times.  Here a wave owns 16 rows (one
+// MFMA column group) and streams them a period at a time (8 blocks: 272
+// bytes, 17 aligned 16-byte chunks of each row) into a ring of LDS stages by
+// 16-byte DMA (buffer_load_dwordx4 ... lds), which reads each row's period
+// contiguously; the lanes then read their words and scales in the operand
+// layout straight from the stage, so no ds_bpermute is needed.  Rows must be
+// whole periods (K a multiple of 640 for pn3t, 512 for pn4t) and 16-byte
+// aligned.  The activations are staged per workgroup as in gemm_stream, in
+// the LDS the ring leaves free; chunk boundaries fall on periods.
+//
+// Stage layout: row r's period at byte 272 r (DMA slot 17 r + c holds its
+// chunk c).  In each block pair (68 bytes = 17 dwords D) the first block's
+// scale is the low half of D[0] and its word j is D[j..j+1] shifted by 16
+// bits; the second block's scale is the high half of D[8] and its word j is
+// D[9 + j].  Lane (gm, jm) takes row jm and the block's words 2gm, 2gm + 1,
+// the same k-group as gemm_stream's operand layout.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kDmRows = 16;                              // rows per wave
+constexpr int kDmTileRows = kSmWaves * kDmRows;          // rows per workgroup tile
+constexpr int kDmChunks = 17;                            // 16-byte chunks per row and period
+constexpr int kDmDma = (kDmRows * kDmChunks + 63) / 64;  // DMA instructions per stage (5)
+constexpr int kDmStage = 1024 * kDmDma;                  // LDS bytes per stage
+#ifndef PN_SM_DMA_STAGES
+#define PN_SM_DMA_STAGES 2
+#endif
+constexpr int kDmNS = PN_SM_DMA_STAGES;                  // stages per wave
+// Tiles a workgroup takes per step of the grid stride: four consecutive
+// tiles (512 rows, usually of one problem) share one activation staging;
+// measured on the M = 8 sweep: 1 tile 2.83 ms, 2 tiles 2.71-2.76, 4 tiles
+// 2.64-2.71 (two stages per wave; three leave too little LDS for the
+// activations: 3.03 ms).
+#ifndef PN_SM_DMA_GROUP
+#define PN_SM_DMA_GROUP 4
+#endif
+constexpr int kDmGroup = PN_SM_DMA_GROUP;                // consecutive tiles per grid-stride step
+constexpr int kDmRing = kSmWaves * kDmNS * kDmStage;     // 80 KiB with two stages
+constexpr int kDmLdsX = kSmLdsMax - kDmRing;             // activation chunk budget
+static_assert(kDmNS >= 1 && kDmNS <= 3, "stages per wave");
+
+template <int TYPE>
+__device__ __forceinline__ void dm_tile(const SmProb &p, int row0, uint8_t *lds, uint8_t *ring)
+{
+    constexpr int P = Unpack<TYPE>::kPairs;
+    const int lane = threadIdx.x & 63;
+    const int jm = lane & 15, gm = lane >> 4;  // operand layout: row jm, k-group gm
+    const int nb = uniform(p.nb), cb = uniform(p.cb), M = uniform(p.M);
+    const int nper = nb >> 3;
+    const uint32_t stride = (uint32_t)uniform(p.stride);
+    const int S = 34 * nb;
+    const int valid = uniform(p.N - row0 < kDmRows ? p.N - row0 : kDmRows);  // <= 0: no rows
+    // rows past N read zeros (offsets past the resource) and are not stored
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(uniform_ptr(p.W + (size_t)(valid > 0 ? row0 : 0) * S),
+                                                valid > 0 ? (uint32_t)valid * (uint32_t)S : 0u);
+    uint32_t vo[kDmDma];
+#pragma unroll
+    for (int i = 0; i < kDmDma; ++i) {
+        const uint32_t q = 64u * i + (uint32_t)lane, r = q / kDmChunks, c = q - kDmChunks * r;
+        vo[i] = r < (uint32_t)kDmRows ? r * (uint32_t)S + 16u * c : 0x80000000u;
+    }
+    const uint32_t ma = jm < M ? (uint32_t)jm : 0u;  // A row; rows >= M are discarded
+    float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto issue = [&](int per) {
+        uint8_t *st = ring + (per % kDmNS) * kDmStage;
+#pragma unroll
+        for (int i = 0; i < kDmDma; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(st + 1024 * i), 16, (int)vo[i], 272 * per, 0, 0);
+    };
+
+    int cbase = 0;                      // first block of the staged chunk
+    int cnext = cb < nb ? cb : nb + 1;  // block at which the next chunk is staged
+    for (int q = 0; q < kDmNS && q < nper; ++q) issue(q);
+    // One period.  LATER: stages issued after this one (a compile-time count,
+    // so that the wait is one instruction).
+    auto period = [&](int per, auto later_c) {
+        constexpr int LATER = decltype(later_c)::value;
+        const int b0 = 8 * per;
+        if (b0 == cnext) {
+            // every wave of the workgroup is on this problem and period
+            __syncthreads();
+            stage_chunk<TYPE>(p, b0, nb - b0 < cb ? nb - b0 : cb, lds);
+            // (the staging loads are younger than the ring's DMA, so the ring
+            // has landed too; saying so on every path keeps the compiler from
+            // draining the ring at every period for loads it thinks pending)
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+            __syncthreads();
+            cbase = b0;
+            cnext = b0 + cb;
+        }
+        __builtin_amdgcn_s_waitcnt(0x0f70 | (LATER * kDmDma));  // vmcnt(LATER * kDmDma)
+        // the lane's words and scales of the period: per block pair, D[2gm ..
+        // 2gm + 2], D[9 + 2gm], D[10 + 2gm], D[0], D[8]
+        const uint8_t *st = ring + (per % kDmNS) * kDmStage;
+        const uint32_t *rw = (const uint32_t *)(st + 272 * jm);
+        uint32_t wa[4][3], wb[4][2], sa[4], sb[4];
+#pragma unroll
+        for (int bp = 0; bp < 4; ++bp) {
+#pragma unroll
+            for (int j = 0; j < 3; ++j) wa[bp][j] = rw[17 * bp + 2 * gm + j];
+            wb[bp][0] = rw[17 * bp + 9 + 2 * gm];
+            wb[bp][1] = rw[17 * bp + 10 + 2 * gm];
+            sa[bp] = rw[17 * bp];
+            sb[bp] = rw[17 * bp + 8];
+        }
+        // the stage is refilled once its reads have landed
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        asm volatile("" ::: "memory");
+        if (per + kDmNS < nper) issue(per + kDmNS);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const int bp = b >> 1;
+            uint32_t w0, w1, sc;
+            if (b & 1) {
+                w0 = wb[bp][0];
+                w1 = wb[bp][1];
+                sc = sb[bp] >> 16;
+            } else {
+                w0 = __builtin_amdgcn_alignbit(wa[bp][1], wa[bp][0], 16);
+                w1 = __builtin_amdgcn_alignbit(wa[bp][2], wa[bp][1], 16);
+                sc = sa[bp] & 0xffffu;
+            }
+            half2_t u[P], v[P];
+            Unpack<TYPE>::run(w0, u);
+            Unpack<TYPE>::run(w1, v);
+            const float d = half_bits_to_float(sc);
+            const uint32_t bl = (uint32_t)(b0 + b - cbase);
+            float4_t D;
+            if constexpr (TYPE == 0) {
+                half4_t a[5];
+#pragma unroll
+                for (int s5 = 0; s5 < 5; ++s5)
+                    a[s5] = __builtin_bit_cast(
+                        half4_t, *(const u32x2 *)(lds + xoff<0>(ma, stride, 160u * bl + 40u * gm + 8u * s5)));
+                // pairs 0..4 from word 2gm, 5..9 from word 2gm + 1; step s takes pairs 2s, 2s + 1
+                D = __builtin_amdgcn_mfma_f32_16x16x16f16(a[0], __builtin_shufflevector(u[0], u[1], 0, 1, 2, 3),
+                                                          (float4_t){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                D = __builtin_amdgcn_mfma_f32_16x16x16f16(a[1], __builtin_shufflevector(u[2], u[3], 0, 1, 2, 3), D, 0, 0, 0);
+                D = __builtin_amdgcn_mfma_f32_16x16x16f16(a[2], __builtin_shufflevector(u[4], v[0], 0, 1, 2, 3), D, 0, 0, 0);
+                D = __builtin_amdgcn_mfma_f32_16x16x16f16(a[3], __builtin_shufflevector(v[1], v[2], 0, 1, 2, 3), D, 0, 0, 0);
+                D = __builtin_amdgcn_mfma_f32_16x16x16f16(a[4], __builtin_shufflevector(v[3], v[4], 0, 1, 2, 3), D, 0, 0, 0);
+            } else {
+                half8_t a[2];
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+                    a[s2] = __builtin_bit_cast(
+                        half8_t, *(const u32x4 *)(lds + xoff<1>(ma, stride, 128u * bl + 32u * gm + 16u * s2)));
+                const half8_t b0v = __builtin_shufflevector(__builtin_shufflevector(u[0], u[1], 0, 1, 2, 3),
+                                                            __builtin_shufflevector(u[2], u[3], 0, 1, 2, 3), 0, 1,
+                                                            2, 3, 4, 5, 6, 7);
+                const half8_t b1v = __builtin_shufflevector(__builtin_shufflevector(v[0], v[1], 0, 1, 2, 3),
+                                                            __builtin_shufflevector(v[2], v[3], 0, 1, 2, 3), 0, 1,
+                                                            2, 3, 4, 5, 6, 7);
+                D = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], b0v, (float4_t){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                D = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[1], b1v, D, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(D[i], d, acc[i]);
+        }
+    };
+    int per = 0;
+    for (; per + kDmNS - 1 < nper; ++per) period(per, std::integral_constant<int, kDmNS - 1>());
+    if constexpr (kDmNS >= 3)
+        if (per + 1 < nper) period(per++, std::integral_constant<int, 1>());
+    if (per < nper) period(per, std::integral_constant<int, 0>());
+    // lane (jm, gm) holds D[m = 4gm + i][row jm]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = 4 * gm + i;
+        if (m < M && jm < valid) p.Y[p.ldy * m + row0 + jm] = acc[i];
+    }
+    // no DMA or store may be outstanding when the next tile reuses the ring
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+}
+
+// Workgroups take tiles (kSmWaves x 16 rows of one problem) in a grid
+// stride, as gemm_stream does; the ring sits above the activation chunk.
+__global__ __launch_bounds__(kSmThreads) void gemm_rows(SmArgs args)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int wave = uniform(threadIdx.x >> 6);
+    uint8_t *ring = lds + kDmLdsX + wave * kDmNS * kDmStage;
+    int i = 0, next0 = -1, staged = -1;
+    SmProb p;
+    // kDmGroup consecutive tiles per step of the grid stride: the activations
+    // staged for a problem serve all of its tiles in the group
+    const int groups = (args.total_tiles + kDmGroup - 1) / kDmGroup;
+    for (int gi = blockIdx.x; gi < groups; gi += gridDim.x)
+    for (int tile = gi * kDmGroup; tile < (gi + 1) * kDmGroup && tile < args.total_tiles; ++tile) {
+        if (tile >= next0) sm_next_problem(args, tile, i, next0, p);
+        if (p.nchunks > 1 || staged != i) {
+            const int nbc = p.nb < p.cb ? p.nb : p.cb;
+            __syncthreads();
+            if (p.type == 0)
+                stage_chunk<0>(p, 0, nbc, lds);
+            else
+                stage_chunk<1>(p, 0, nbc, lds);
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0), on every path (see dm_tile)
+            __syncthreads();
+        }
+        staged = p.nchunks > 1 ? -1 : i;
+        const int row0 = ((tile - p.tile0) * kSmWaves + wave) * kDmRows;
+        if (p.type == 0)
+            dm_tile<0>(p, row0, lds, ring);
+        else
+            dm_tile<1>(p, row0, lds, ring);
     }
 }
 
@@ -507,6 +732,7 @@ int sm_wgs_per_cu(bool mfma, int lds)
                                   kSmLdsMax);
         (void)hipFuncSetAttribute((const void *)gemm_stream<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                   kSmLdsMax);
+        (void)hipFuncSetAttribute((const void *)gemm_rows, hipFuncAttributeMaxDynamicSharedMemorySize, kSmLdsMax);
         d.ready = 1;
     }
     int q = (lds + 1023) / 1024;
@@ -524,11 +750,24 @@ int sm_wgs_per_cu(bool mfma, int lds)
     return o;
 }
 
+// Can gemm_rows take this problem?  Rows of whole periods (K a multiple of
+// 640 for pn3t, 512 for pn4t), W 16-byte aligned, 16-row offsets within the
+// kernel's 32-bit arithmetic, the MFMA arithmetic, and a kernel choice that
+// allows it (pn_set_gemv_kernel: anything but PN_GEMV_STREAM).
+bool sm_dma_ok(int t, const void *W, int64_t K, bool mfma)
+{
+    if (!mfma || pn_get_gemv_kernel() == PN_GEMV_STREAM) return false;
+    if (((uintptr_t)W & 15) != 0) return false;
+    const int64_t nb = K / wpb(t);
+    return nb % 8 == 0 && nb * 34 * kDmRows <= INT32_MAX;
+}
+
 // Fill an SmProb for one problem (validated) and choose its activation
 // chunking: the fewest chunks of whole blocks whose M staged rows fit the LDS
-// budget, equal in size up to U blocks (every boundary a multiple of U).
+// budget, equal in size up to U blocks (every boundary a multiple of U), or
+// up to periods for gemm_rows (dma), whose ring takes part of the LDS.
 pn_status sm_make(int t, const void *W, int64_t N, int64_t K, const void *X, int64_t ldx, int M, float *Y,
-                  int64_t ldy, bool mfma, SmProb &p)
+                  int64_t ldy, bool mfma, bool dma, SmProb &p)
 {
     pn_status st = check_matrix(t, W, N, K);
     if (st) return st;
@@ -539,13 +778,15 @@ pn_status sm_make(int t, const void *W, int64_t N, int64_t K, const void *X, int
     const int64_t nb = K / wpb(t);
     if (nb * 34 * kWaveRows > INT32_MAX) return PN_EUNSUPPORTED;  // per-wave offsets are 32-bit
     const int64_t bytes_per_block = (int64_t)wpb(t) * 2;              // staged bytes per block and row
+    const int64_t unit = dma ? 8 : kSmU;  // chunk boundaries at multiples of this many blocks
+    const int64_t budget = dma ? kDmLdsX : mfma ? kSmLdsMax : kSmLdsValu;
     int64_t nchunks = 1, cb = nb, stride = 0;
     for (;; ++nchunks) {
         cb = (nb + nchunks - 1) / nchunks;
-        if (cb < nb) cb = (cb + kSmU - 1) / kSmU * kSmU;  // chunk boundaries at multiples of U blocks
+        if (cb < nb) cb = (cb + unit - 1) / unit * unit;
         stride = (cb * bytes_per_block + 255) / 256 * 256;
-        if (stride * M <= (mfma ? kSmLdsMax : kSmLdsValu)) break;
-        if (cb <= kSmU) return PN_EUNSUPPORTED;
+        if (stride * M <= budget) break;
+        if (cb <= unit) return PN_EUNSUPPORTED;
     }
     memset(&p, 0, sizeof(p));
     p.W = (const uint8_t *)W;
@@ -565,12 +806,15 @@ pn_status sm_make(int t, const void *W, int64_t N, int64_t K, const void *X, int
 
 int sm_lds(const SmProb &p) { return p.M * p.stride; }
 
-pn_status sm_launch(const SmArgs &a, int lds, bool mfma, hipStream_t s, int variant)
+pn_status sm_launch(const SmArgs &a, int lds, bool mfma, bool dma, hipStream_t s, int variant)
 {
-    int grid = device_cus() * sm_wgs_per_cu(mfma, lds);
+    int grid = device_cus() * (dma ? 1 : sm_wgs_per_cu(mfma, lds));  // gemm_rows takes the whole LDS
     if (grid > a.total_tiles) grid = a.total_tiles;
     if (grid < 1) grid = 1;
-    if (mfma)
+    if (dma) {
+        (void)sm_wgs_per_cu(true, lds);  // raises the kernels' LDS limit once per device
+        hipLaunchKernelGGL(gemm_rows, dim3(grid), dim3(kSmThreads), kSmLdsMax, s, a);
+    } else if (mfma)
         hipLaunchKernelGGL(gemm_stream<true>, dim3(grid), dim3(kSmThreads), lds, s, a);
     else
         hipLaunchKernelGGL(gemm_stream<false>, dim3(grid), dim3(kSmThreads), lds, s, a);
@@ -588,8 +832,10 @@ pn_status pn::host::smallm_group_run(const pn_group *g, hipStream_t s)
     a.table = (const SmProb *)g->table;
     a.count = g->count;
     a.total_tiles = g->total_tiles;
-    const bool mfma = g->flags == PN_SMALLM_MFMA;
-    return sm_launch(a, g->lds, mfma, s, mfma ? kVarGroupSmallMMfma : kVarGroupSmallMValu);
+    const bool mfma = (g->flags & 0xf) == PN_SMALLM_MFMA;
+    const bool dma = (g->flags & kSmFlagDma) != 0;
+    return sm_launch(a, g->lds, mfma, dma, s,
+                     dma ? kVarGroupSmallMRows : mfma ? kVarGroupSmallMMfma : kVarGroupSmallMValu);
 }
 
 extern "C" {
@@ -609,12 +855,14 @@ pn_status pn_gemm_smallm(pn_type t, const void *W, int64_t N, int64_t K, const v
     SmArgs a;
     memset(&a, 0, sizeof(a));
     const bool mfma = pn_get_smallm_math() == PN_SMALLM_MFMA;
-    pn_status st = sm_make(t, W, N, K, X, ldx, M, Y, ldy, mfma, a.p0);
+    const bool dma = type_ok(t) && W && K >= wpb(t) && sm_dma_ok(t, W, K, mfma);
+    pn_status st = sm_make(t, W, N, K, X, ldx, M, Y, ldy, mfma, dma, a.p0);
     if (st) return st;
-    const int64_t tiles = (N + kTileRows - 1) / kTileRows;
+    const int64_t rows = dma ? kDmTileRows : kTileRows;
     a.count = 1;
-    a.total_tiles = (int32_t)tiles;
-    return sm_launch(a, sm_lds(a.p0), mfma, (hipStream_t)stream, mfma ? kVarSmallMMfma : kVarSmallMValu);
+    a.total_tiles = (int32_t)((N + rows - 1) / rows);
+    return sm_launch(a, sm_lds(a.p0), mfma, dma, (hipStream_t)stream,
+                     dma ? kVarSmallMRows : mfma ? kVarSmallMMfma : kVarSmallMValu);
 }
 
 pn_status pn_group_create_smallm(const pn_gemm_desc *descs, int count, pn_group **out)
@@ -627,12 +875,19 @@ pn_status pn_group_create_smallm(const pn_gemm_desc *descs, int count, pn_group 
     int64_t tiles = 0;
     pn_status st = PN_OK;
     const int math = pn_get_smallm_math();
+    // gemm_rows runs the plan if it takes every problem (one launch, one kernel)
+    bool dma = true;
+    for (int i = 0; i < count && dma; ++i) {
+        const pn_gemm_desc &e = descs[i];
+        dma = type_ok(e.type) && e.W && e.K >= wpb(e.type) && sm_dma_ok(e.type, e.W, e.K, math == PN_SMALLM_MFMA);
+    }
+    const int64_t rows = dma ? kDmTileRows : kTileRows;
     for (int i = 0; i < count && st == PN_OK; ++i) {
         const pn_gemm_desc &e = descs[i];
-        st = sm_make(e.type, e.W, e.N, e.K, e.X, e.ldx, e.M, e.Y, e.ldy, math == PN_SMALLM_MFMA, host[i]);
+        st = sm_make(e.type, e.W, e.N, e.K, e.X, e.ldx, e.M, e.Y, e.ldy, math == PN_SMALLM_MFMA, dma, host[i]);
         if (st != PN_OK) break;
         host[i].tile0 = (int32_t)tiles;
-        tiles += (e.N + kTileRows - 1) / kTileRows;
+        tiles += (e.N + rows - 1) / rows;
         if (tiles > INT32_MAX) st = PN_EUNSUPPORTED;
         if (sm_lds(host[i]) > lds) lds = sm_lds(host[i]);
     }
@@ -661,7 +916,7 @@ pn_status pn_group_create_smallm(const pn_gemm_desc *descs, int count, pn_group 
     g->count = count;
     g->total_tiles = (int)tiles;
     g->lds = lds;
-    g->flags = math;
+    g->flags = math | (dma ? kSmFlagDma : 0);
     *out = g;
     return PN_OK;
 }

@@ -87,7 +87,11 @@ pn_status pn_gemv2(pn_type t, const void *W0, const void *W1, int64_t N,
  *       ldx even
  *   Y : M rows of fp32, leading dimension ldy >= N (elements), overwritten
  *   M : 1..16
- * The arithmetic unit is the one pn_set_smallm_math selected. */
+ * The arithmetic unit is the one pn_set_smallm_math selected.  With MFMA,
+ * rows of whole 8-block periods (K a multiple of 640 for pn3t, 512 for pn4t)
+ * and a 16-byte-aligned W are streamed into LDS by DMA (kernel gemm_rows)
+ * unless pn_set_gemv_kernel chose PN_GEMV_STREAM; other problems, and the
+ * VALU arithmetic, use register loads (gemm_stream).  Same accuracy bar. */
 pn_status pn_gemm_smallm(pn_type t, const void *W, int64_t N, int64_t K,
                          const void *X, int64_t ldx, int M,
                          float *Y, int64_t ldy, void *stream);
@@ -125,7 +129,8 @@ typedef enum { PN_SMALLM_MFMA = 0, PN_SMALLM_VALU = 1 } pn_smallm_math;
 pn_status pn_set_smallm_math(pn_smallm_math m);
 pn_smallm_math pn_get_smallm_math(void);
 
-/* Which kernel runs the M = 1 products (pn_gemv, pn_gemv2 and pn_group_*):
+/* Which kernel runs the M = 1 products (pn_gemv, pn_gemv2 and pn_group_*;
+ * for the small-batch products see pn_gemm_smallm):
  *   PN_GEMV_AUTO    the row-tile kernel where it applies and the launch is
  *                   large enough, else the register-pipeline kernel; the
  *                   default.  The row-tile kernel applies to rows of whole

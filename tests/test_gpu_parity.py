@@ -341,21 +341,37 @@ def test_group(gemv_kernel, which):
 # ---------------------------------------------------------------------------
 # small M (both arithmetic units over the same loads)
 # ---------------------------------------------------------------------------
-MATHS = ["mfma", "valu"]
-# (type, N, K): several 32-row wave tiles with ragged tails, rows shorter than
-# the 2U-block pipeline (1 and 7 blocks), rows for the in-order U-slot
-# pipeline (9 and 11 blocks: at least 2U, fewer than the grouped pipeline's
-# 4U), and activations that take several LDS chunks at M = 8 (pn3t K = 5120:
-# 2 chunks; pn4t K = 17408: 5 chunks).
+# The three small-M paths: MFMA arithmetic with the kernel choice left to the
+# library (gemm_rows, weights staged through LDS by DMA, wherever the rows
+# are whole 8-block periods; gemm_stream elsewhere), MFMA on gemm_stream
+# forced, and the VALU arithmetic (gemm_stream).
+MATHS = ["mfma", "mfma_stream", "valu"]
+# (type, N, K): several 32-row (gemm_stream) and 16-row (gemm_rows) wave tiles
+# with ragged tails; rows shorter than the 2U-block pipeline (1 and 7
+# blocks), rows for the in-order U-slot pipeline (9 and 11 blocks: at least
+# 2U, fewer than the grouped pipeline's 4U); rows of one period (8 blocks);
+# and activations that take several LDS chunks at M = 8 (pn3t K = 5120: 2
+# chunks for gemm_stream at M = 16, 2 for gemm_rows from M = 9; pn4t K = 17408:
+# several for both).
 SMALLM_SHAPES = [("pn3t", 256, 5120), ("pn4t", 300, 17408), ("pn4t", 33, 6144), ("pn3t", 7, 80),
-                 ("pn4t", 19, 64 * 9), ("pn3t", 45, 80 * 7), ("pn3t", 40, 80 * 11), ("pn4t", 1000, 5120)]
+                 ("pn4t", 19, 64 * 9), ("pn3t", 45, 80 * 7), ("pn3t", 40, 80 * 11), ("pn4t", 1000, 5120),
+                 ("pn3t", 130, 640), ("pn4t", 17, 512), ("pn3t", 129, 640 * 3)]
+
+
+def smallm_variant(path, t, k, group=False):
+    """The kernel the library picks for a problem on this path."""
+    rows = path == "mfma" and (k // WPB[t]) % 8 == 0
+    name = "gemm_rows_mfma" if rows else "gemm_stream_" + ("valu" if path == "valu" else "mfma")
+    return name + ("_group" if group else "")
 
 
 @pytest.fixture
 def smallm_math(request):
-    B.pn_set_smallm_math(request.param)
+    B.pn_set_smallm_math("valu" if request.param == "valu" else "mfma")
+    B.pn_set_gemv_kernel("stream" if request.param == "mfma_stream" else "auto")
     yield request.param
     B.pn_set_smallm_math("mfma")
+    B.pn_set_gemv_kernel("auto")
 
 
 def gpu_smallm(t, w, n, k, X, m, ldx, ldy):
@@ -375,7 +391,7 @@ def test_gemm_smallm(smallm_math, t, n, k, m):
     X[:, :k] = synth.activation(g, k, m)
     say("gemm_smallm %s %s %dx%d M=%d" % (smallm_math, t, n, k, m))
     Y = gpu_smallm(t, w, n, k, X, m, ldx, ldy)
-    assert B.pn_variant_name(B.pn_last_variant()) == "gemm_stream_" + smallm_math
+    assert B.pn_variant_name(B.pn_last_variant()) == smallm_variant(smallm_math, t, k)
     assert np.all(Y[:, n:] == 7.0), "wrote past N in a row of Y"
     y64, a = pnref.gemm_f64(t, w, n, k, X[:, :k])
     assert_gemv_close(Y[:, :n], y64, a, "smallm %s %s M=%d" % (smallm_math, t, m))
@@ -387,21 +403,27 @@ def test_gemm_smallm(smallm_math, t, n, k, m):
 
 @pytest.mark.parametrize("smallm_math", MATHS, indirect=True)
 @pytest.mark.parametrize("t", ["pn3t", "pn4t"])
-def test_smallm_one_hot_exact(smallm_math, t):
+@pytest.mark.parametrize("nblk", [6, 16])
+def test_smallm_one_hot_exact(smallm_math, t, nblk):
     """Row m of X is one-hot at k_m: Y[m, r] = w[r, k_m] exactly (one exact
     product, the rest zeros).  Pins the k <-> (block, word, slot) map of the
     operand layouts, including both words of a lane, the block edges and all
-    16 batch rows."""
+    16 batch rows; with 16 blocks (two periods) also both blocks of a pair in
+    gemm_rows's stage (the first block's words lie off the dword grid)."""
     wpb = WPB[t]
-    n, k = 70, wpb * 6
+    n, k = 70, wpb * nblk
     w, _ = random_matrix(17, t, n, k)
     ks = [0, 1, wpb // 4 - 1, wpb // 4, wpb // 2 + 3, wpb - 1, wpb, 5 * wpb + wpb - 2,
           2, wpb // 8, wpb // 4 + 7, wpb // 2 - 1, wpb // 2, 3 * wpb // 4, 2 * wpb + 9, 4 * wpb - 1]
+    if nblk == 16:
+        ks[8:] = [3 * wpb + 11, 7 * wpb + wpb - 1, 8 * wpb, 9 * wpb + 21, 11 * wpb + 40, 12 * wpb + 5,
+                  14 * wpb + 63, 16 * wpb - 1]
     X = np.zeros((16, k), np.float16)
     for m, km in enumerate(ks):
         X[m, km] = 1.0
-    say("smallm one-hot %s %s" % (smallm_math, t))
+    say("smallm one-hot %s %s %d blocks" % (smallm_math, t, nblk))
     Y = gpu_smallm(t, w, n, k, X, 16, k, n)
+    assert B.pn_variant_name(B.pn_last_variant()) == smallm_variant(smallm_math, t, k)
     dense = pnref.dequantize(t, w, n, k)
     for m, km in enumerate(ks):
         assert_bits_equal(Y[m] + 0.0, dense[:, km] + 0.0, "one-hot m=%d k=%d" % (m, km))
@@ -439,7 +461,39 @@ def test_smallm_group(smallm_math):
     grp = B.Group(probs, smallm=True)
     grp.run()
     sync()
-    assert B.pn_variant_name(B.pn_last_variant()) == "gemm_stream_%s_group" % smallm_math
+    # one problem (K = 80, 720) is not whole periods: the plan runs on gemm_stream
+    assert B.pn_variant_name(B.pn_last_variant()) == smallm_variant(smallm_math, "pn3t", 80, group=True)
+    for t, w, n, k, X, Y in host:
+        Yh = Y.cpu().numpy()
+        assert np.all(Yh[:, n:] == 7.0)
+        y64, a = pnref.gemm_f64(t, w, n, k, X)
+        assert_gemv_close(Yh[:, :n], y64, a, "smallm group %s %dx%d M=%d" % (t, n, k, X.shape[0]))
+    grp.close()
+
+
+@pytest.mark.parametrize("smallm_math", MATHS, indirect=True)
+def test_smallm_group_periods(smallm_math):
+    """A plan whose problems are all whole periods (gemm_rows runs it with the
+    MFMA arithmetic): mixed types, M, leading dimensions, ragged N against the
+    16-row waves and 128-row tiles, one- and many-chunk activations."""
+    specs = [("pn3t", 6144 // 16 + 5, 5120, 8), ("pn4t", 1024 + 3, 5120, 16), ("pn4t", 200, 17408, 8),
+             ("pn3t", 17, 640, 1), ("pn4t", 130, 6144, 5), ("pn3t", 2, 1280, 12)]
+    host, probs, keep = [], [], []
+    for i, (t, n, k, m) in enumerate(specs):
+        w, g = random_matrix(2000 + i, t, n, k)
+        ldx, ldy = k + 8 * (i % 2), n + 2 * (i % 3)
+        X = np.zeros((m, ldx), np.float16)
+        X[:, :k] = synth.activation(g, k, m)
+        Y = torch.full((m, ldy), 7.0, dtype=torch.float32, device="cuda")
+        wd, xd = dev(w), dev(X)
+        keep += [wd, xd]
+        probs.append((t, wd, n, k, xd, ldx, m, Y, ldy))
+        host.append((t, w, n, k, X[:, :k], Y))
+    say("smallm group of whole periods %s: %d problems" % (smallm_math, len(specs)))
+    grp = B.Group(probs, smallm=True)
+    grp.run()
+    sync()
+    assert B.pn_variant_name(B.pn_last_variant()) == smallm_variant(smallm_math, "pn3t", 640, group=True)
     for t, w, n, k, X, Y in host:
         Yh = Y.cpu().numpy()
         assert np.all(Yh[:, n:] == 7.0)

@@ -86,13 +86,17 @@ def sweep_m8():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("math", ["mfma", "valu"])
+@pytest.mark.parametrize("math", ["mfma", "mfma_stream", "valu"])
 def test_sweep_m8(sweep_m8, math):
     """M = 8 over the full sweep: one grouped launch per token (the benchmark's
-    configuration) and one launch per matrix, with the given arithmetic."""
+    configuration) and one launch per matrix, with the given arithmetic (and
+    for MFMA, the library's kernel choice, gemm_rows for these shapes, or
+    gemm_stream forced)."""
     sw, store = sweep_m8
-    B.pn_set_smallm_math(math)
+    B.pn_set_smallm_math("valu" if math == "valu" else "mfma")
+    B.pn_set_gemv_kernel("stream" if math == "mfma_stream" else "auto")
     sw.close()  # plans keep the arithmetic they were created with
+    kernel = "gemm_rows_mfma" if math == "mfma" else "gemm_stream_" + ("valu" if math == "valu" else "mfma")
     try:
         for schedule in ("token", "gemv"):
             for e in sw.mats:
@@ -100,8 +104,10 @@ def test_sweep_m8(sweep_m8, math):
             say("sweep M=8 %s schedule %s" % (math, schedule))
             sw.step(schedule)
             sync()
+            assert B.pn_variant_name(B.pn_last_variant()) == kernel + ("_group" if schedule == "token" else "")
             worst = _check_samples(sw, store, m=8)
             say("sweep M=8 %s %s: worst %.3g" % (math, schedule, worst))
     finally:
         B.pn_set_smallm_math("mfma")
+        B.pn_set_gemv_kernel("auto")
         sw.close()
