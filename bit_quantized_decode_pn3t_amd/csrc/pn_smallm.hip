@@ -125,7 +125,7 @@ __device__ __forceinline__ uint32_t xoff(uint32_t m, uint32_t stride, uint32_t o
 // loads makes the compiler's wait analysis drain every load in flight at the
 // pipeline's loop head.  Each thread issues up to kStageBatch loads before it
 // writes any of them (one memory round trip per batch, not per piece).
-template <int TYPE>
+template <int TYPE, int NT = kSmThreads>
 __device__ __forceinline__ void stage_chunk(const SmProb &p, int b0, int nbc, uint8_t *lds)
 {
     constexpr int W = Fmt<TYPE>::W;
@@ -135,18 +135,18 @@ __device__ __forceinline__ void stage_chunk(const SmProb &p, int b0, int nbc, ui
     const __amdgpu_buffer_rsrc_t xr =
         make_rsrc(uniform_ptr(p.X + (size_t)2 * b0 * W), (uint32_t)(row_stride * (p.M - 1) + 16 * per_row));
     constexpr int kStageBatch = 4;
-    for (int i0 = 0; i0 < total; i0 += kStageBatch * kSmThreads) {
+    for (int i0 = 0; i0 < total; i0 += kStageBatch * NT) {
         u32x4 v[kStageBatch];
 #pragma unroll
         for (int k = 0; k < kStageBatch; ++k) {
-            const int i = i0 + k * kSmThreads + (int)threadIdx.x;
+            const int i = i0 + k * NT + (int)threadIdx.x;
             const int m = i / per_row, q = i - m * per_row;
             // pieces past the end read zeros (offset past the resource) and are not written
             v[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, row_stride * m + 16 * q, 0, 0));
         }
 #pragma unroll
         for (int k = 0; k < kStageBatch; ++k) {
-            const int i = i0 + k * kSmThreads + (int)threadIdx.x;
+            const int i = i0 + k * NT + (int)threadIdx.x;
             const int m = i / per_row, q = i - m * per_row;
             if (i < total) *(u32x4 *)(lds + xoff<TYPE>((uint32_t)m, (uint32_t)p.stride, 16u * q)) = v[k];
         }
@@ -500,10 +500,11 @@ __global__ __launch_bounds__(kSmThreads) void gemm_stream(SmArgs args)
 // even with its arithmetic taken out: each request carries 32 bytes and
 // every 128-byte line is requested four times.  Here a wave owns 16 rows (one
 // MFMA column group) and streams them a period at a time (8 blocks: 272
-// bytes, 17 aligned 16-byte chunks of each row) into a ring of LDS stages by
-// 16-byte DMA (buffer_load_dwordx4 ... lds), which reads each row's period
+// bytes, 17 aligned 16-byte chunks of each row) into an LDS stage by 16-byte
+// DMA (buffer_load_dwordx4 ... lds), which reads each row's period
 // contiguously; the lanes then read their words and scales in the operand
-// layout straight from the stage, so no ds_bpermute is needed.  Rows must be
+// layout straight from the stage, so no ds_bpermute is needed, and the stage
+// is refilled with the next period while they compute.  Rows must be
 // whole periods (K a multiple of 640 for pn3t, 512 for pn4t) and 16-byte
 // aligned.  The activations are staged per workgroup as in gemm_stream, in
 // the LDS the ring leaves free; chunk boundaries fall on periods.
@@ -517,27 +518,37 @@ __global__ __launch_bounds__(kSmThreads) void gemm_stream(SmArgs args)
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Waves per workgroup and ring stages per wave (measured on the M = 8 sweep):
+// 16 waves with one stage each (a wave reads its stage into registers and
+// refills it at once, so that one period is in flight while it computes;
+// four waves per SIMD hide each other's latencies) 2.41-2.51 ms; 8 waves
+// with two stages 2.66-2.68 ms, with one 2.60; 12 waves with one 2.63.
+// Three stages leave too little LDS for the activations (3.03 ms).
+#ifndef PN_SM_DMA_WAVES
+#define PN_SM_DMA_WAVES 16
+#endif
+#ifndef PN_SM_DMA_STAGES
+#define PN_SM_DMA_STAGES 1
+#endif
+// Tiles a workgroup takes per step of the grid stride: consecutive tiles
+// (usually of one problem) share one activation staging.  Measured on the
+// M = 8 sweep with 16 waves (256-row tiles): 1 tile 2.54 ms, 2 tiles 2.46, 4
+// tiles 2.51, 8 tiles 2.63.
+#ifndef PN_SM_DMA_GROUP
+#define PN_SM_DMA_GROUP 2
+#endif
 constexpr int kDmRows = 16;                              // rows per wave
-constexpr int kDmTileRows = kSmWaves * kDmRows;          // rows per workgroup tile
+constexpr int kDmWaves = PN_SM_DMA_WAVES;                // waves per workgroup (one workgroup per CU)
+constexpr int kDmThreads = 64 * kDmWaves;
+constexpr int kDmTileRows = kDmWaves * kDmRows;          // rows per workgroup tile
 constexpr int kDmChunks = 17;                            // 16-byte chunks per row and period
 constexpr int kDmDma = (kDmRows * kDmChunks + 63) / 64;  // DMA instructions per stage (5)
 constexpr int kDmStage = 1024 * kDmDma;                  // LDS bytes per stage
-#ifndef PN_SM_DMA_STAGES
-#define PN_SM_DMA_STAGES 2
-#endif
 constexpr int kDmNS = PN_SM_DMA_STAGES;                  // stages per wave
-// Tiles a workgroup takes per step of the grid stride: four consecutive
-// tiles (512 rows, usually of one problem) share one activation staging;
-// measured on the M = 8 sweep: 1 tile 2.83 ms, 2 tiles 2.71-2.76, 4 tiles
-// 2.64-2.71 (two stages per wave; three leave too little LDS for the
-// activations: 3.03 ms).
-#ifndef PN_SM_DMA_GROUP
-#define PN_SM_DMA_GROUP 4
-#endif
 constexpr int kDmGroup = PN_SM_DMA_GROUP;                // consecutive tiles per grid-stride step
-constexpr int kDmRing = kSmWaves * kDmNS * kDmStage;     // 80 KiB with two stages
+constexpr int kDmRing = kDmWaves * kDmNS * kDmStage;     // 80 KiB
 constexpr int kDmLdsX = kSmLdsMax - kDmRing;             // activation chunk budget
-static_assert(kDmNS >= 1 && kDmNS <= 3, "stages per wave");
+static_assert(kDmNS >= 1 && kDmNS <= 3 && kDmThreads <= 1024 && kDmRing < kSmLdsMax, "ring shape");
 
 template <int TYPE>
 __device__ __forceinline__ void dm_tile(const SmProb &p, int row0, uint8_t *lds, uint8_t *ring)
@@ -580,7 +591,7 @@ __device__ __forceinline__ void dm_tile(const SmProb &p, int row0, uint8_t *lds,
         if (b0 == cnext) {
             // every wave of the workgroup is on this problem and period
             __syncthreads();
-            stage_chunk<TYPE>(p, b0, nb - b0 < cb ? nb - b0 : cb, lds);
+            stage_chunk<TYPE, kDmThreads>(p, b0, nb - b0 < cb ? nb - b0 : cb, lds);
             // (the staging loads are younger than the ring's DMA, so the ring
             // has landed too; saying so on every path keeps the compiler from
             // draining the ring at every period for loads it thinks pending)
@@ -675,9 +686,9 @@ __device__ __forceinline__ void dm_tile(const SmProb &p, int row0, uint8_t *lds,
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 }
 
-// Workgroups take tiles (kSmWaves x 16 rows of one problem) in a grid
+// Workgroups take tiles (kDmWaves x 16 rows of one problem) in a grid
 // stride, as gemm_stream does; the ring sits above the activation chunk.
-__global__ __launch_bounds__(kSmThreads) void gemm_rows(SmArgs args)
+__global__ __launch_bounds__(kDmThreads) void gemm_rows(SmArgs args)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int wave = uniform(threadIdx.x >> 6);
@@ -694,14 +705,14 @@ __global__ __launch_bounds__(kSmThreads) void gemm_rows(SmArgs args)
             const int nbc = p.nb < p.cb ? p.nb : p.cb;
             __syncthreads();
             if (p.type == 0)
-                stage_chunk<0>(p, 0, nbc, lds);
+                stage_chunk<0, kDmThreads>(p, 0, nbc, lds);
             else
-                stage_chunk<1>(p, 0, nbc, lds);
+                stage_chunk<1, kDmThreads>(p, 0, nbc, lds);
             __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0), on every path (see dm_tile)
             __syncthreads();
         }
         staged = p.nchunks > 1 ? -1 : i;
-        const int row0 = ((tile - p.tile0) * kSmWaves + wave) * kDmRows;
+        const int row0 = ((tile - p.tile0) * kDmWaves + wave) * kDmRows;
         if (p.type == 0)
             dm_tile<0>(p, row0, lds, ring);
         else
@@ -813,7 +824,7 @@ pn_status sm_launch(const SmArgs &a, int lds, bool mfma, bool dma, hipStream_t s
     if (grid < 1) grid = 1;
     if (dma) {
         (void)sm_wgs_per_cu(true, lds);  // raises the kernels' LDS limit once per device
-        hipLaunchKernelGGL(gemm_rows, dim3(grid), dim3(kSmThreads), kSmLdsMax, s, a);
+        hipLaunchKernelGGL(gemm_rows, dim3(grid), dim3(kDmThreads), kSmLdsMax, s, a);
     } else if (mfma)
         hipLaunchKernelGGL(gemm_stream<true>, dim3(grid), dim3(kSmThreads), lds, s, a);
     else
