@@ -45,6 +45,20 @@ def test_host_helpers():
     assert B.pn_variant_name(B.pn_last_variant()) == "none"
 
 
+def test_variant_names():
+    """Every kernel the library can report has its own name; unknown ids are
+    reported as such rather than as a kernel."""
+    names = [B.pn_variant_name(v) for v in range(15)]
+    assert names[0] == "none"
+    assert len(set(names)) == len(names), names
+    for expect in ("gemv_rows", "gemv_rows_group", "gemv_stream", "gemv_stream_group", "gemv_generic",
+                   "gemm_stream_mfma", "gemm_stream_valu", "gemm_stream_mfma_group", "gemm_stream_valu_group",
+                   "gemm_rows_mfma", "gemm_rows_mfma_group", "gemm_prefill", "hadamard_rotate", "dequant"):
+        assert expect in names, expect
+    assert B.pn_variant_name(15) not in names[1:]
+    assert B.pn_variant_name(-1) not in names[1:]
+
+
 FAKE = 0x10000  # never dereferenced: every call below fails its host checks
 
 
