@@ -1,8 +1,10 @@
-"""The new entry points under HIP graph capture: a split-K prefill product
-(its zero fill is a kernel, so the call can be captured) and a plan with
-rotated inputs (its rotation launch is replayed with the GEMV launch).  Each
-graph is replayed several times, with eager work and synchronizations
-between the replays, and every replay is checked against the oracle."""
+"""Entry points under HIP graph capture: a split-K prefill product (its zero
+fill is a kernel, so the call can be captured), a plan with rotated inputs
+(its rotation launch is replayed with the GEMV launch), a row-tile M = 1
+plan (its tile counters are reset by the kernel itself) and a small-M plan
+on the DMA kernel.  Each graph is replayed several times, with eager work
+and synchronizations between the replays, and every replay is checked
+against the oracle."""
 import numpy as np
 import pytest
 
@@ -72,4 +74,82 @@ def test_rotated_plan_graph_replays():
             x = p[4].cpu().numpy()
             y64, a = pnref.gemv_f64(t, w, n, k, pnref.rotate(x))
             assert_gemv_close(p[5].cpu().numpy(), y64, a, "rotated plan replay %d %s" % (rep, t))
+    plan.close()
+
+
+def _replay_plan(plan, host, probs, fresh, check, what):
+    """Capture plan.run() and replay it three times; before each replay the
+    inputs are refreshed and the outputs poisoned eagerly."""
+    plan.run()  # warm
+    sync()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        plan.run()
+    sync()
+    for rep in range(3):
+        for h, p in zip(host, probs):
+            fresh(h, p)
+        sync()
+        say("%s graph: replay %d" % (what, rep))
+        gr.replay()
+        sync()
+        for h, p in zip(host, probs):
+            check(h, p, "%s replay %d" % (what, rep))
+
+
+def test_row_tile_plan_graph_replays():
+    """A gemv_rows group plan (pool counters reset by the last wave of each
+    run, so the next replay finds them at zero)."""
+    specs = [("pn3t", 300, 5120), ("pn4t", 100, 17408), ("pn4t", 64, 6144)]
+    host, probs = [], []
+    for i, (t, n, k) in enumerate(specs):
+        g = np.random.default_rng([43, i])
+        w = synth.random_blocks(g, t, n, k)
+        host.append((t, w, n, k, g))
+        probs.append((t, dev(w.reshape(-1)), n, k, dev(synth.activation(g, k)),
+                      torch.empty(n, dtype=torch.float32, device="cuda")))
+    B.pn_set_gemv_kernel("rows")
+    try:
+        plan = B.Group(probs)
+    finally:
+        B.pn_set_gemv_kernel("auto")
+
+    def fresh(h, p):
+        p[4].copy_(dev(synth.activation(h[4], h[3])))
+        p[5].fill_(float("nan"))
+
+    def check(h, p, what):
+        t, w, n, k, _ = h
+        y64, a = pnref.gemv_f64(t, w, n, k, p[4].cpu().numpy())
+        assert_gemv_close(p[5].cpu().numpy(), y64, a, what)
+
+    _replay_plan(plan, host, probs, fresh, check, "row-tile plan")
+    assert B.pn_variant_name(B.pn_last_variant()) == "gemv_rows_group"
+    plan.close()
+
+
+def test_dma_smallm_plan_graph_replays():
+    """A small-M plan run by gemm_rows (weights staged by DMA), M = 8 and 16,
+    one problem with activations restaged in chunks."""
+    specs = [("pn3t", 300, 5120, 8), ("pn4t", 130, 17408, 8), ("pn4t", 64, 6144, 16)]
+    host, probs = [], []
+    for i, (t, n, k, m) in enumerate(specs):
+        g = np.random.default_rng([47, i])
+        w = synth.random_blocks(g, t, n, k)
+        host.append((t, w, n, k, m, g))
+        probs.append((t, dev(w.reshape(-1)), n, k, dev(synth.activation(g, k, m)), k, m,
+                      torch.empty((m, n), dtype=torch.float32, device="cuda"), n))
+    plan = B.Group(probs, smallm=True)
+
+    def fresh(h, p):
+        p[4].copy_(dev(synth.activation(h[5], h[3], h[4])))
+        p[7].fill_(float("nan"))
+
+    def check(h, p, what):
+        t, w, n, k, m, _ = h
+        y64, a = pnref.gemm_f64(t, w, n, k, p[4].cpu().numpy())
+        assert_gemv_close(p[7].cpu().numpy(), y64, a, what)
+
+    _replay_plan(plan, host, probs, fresh, check, "small-M plan")
+    assert B.pn_variant_name(B.pn_last_variant()) == "gemm_rows_mfma_group"
     plan.close()
