@@ -471,6 +471,24 @@ def test_smallm_group(smallm_math):
     grp.close()
 
 
+@pytest.mark.parametrize("smallm_math", ["mfma", "mfma_stream"], indirect=True)
+@pytest.mark.parametrize("t,n,k", [("pn3t", 17408, 5120), ("pn4t", 5120, 17408)])
+def test_smallm_full_size_m16_sampled(smallm_math, t, n, k):
+    """M = 16 (k = 15 drafts) on the gate and down projections at full size:
+    the activations take several LDS chunks per tile on both kernels.  Every
+    output of sampled weight rows (first and last of the tiles and waves, and
+    random ones) against the oracle."""
+    m = 16
+    w, g = random_matrix(n + m, t, n, k)
+    X = synth.activation(g, k, m)
+    say("smallm full size M=16 %s %s %dx%d" % (smallm_math, t, n, k))
+    Y = gpu_smallm(t, w, n, k, X, m, k, n)
+    assert B.pn_variant_name(B.pn_last_variant()) == smallm_variant(smallm_math, t, k)
+    rows = np.array(sorted(set([0, 15, 16, 31, 255, 256, 511, n - 17, n - 1] + list(g.integers(0, n, 7)))))
+    y64, a = pnref.gemm_f64(t, w[rows], len(rows), k, X)
+    assert_gemv_close(Y[:, rows], y64, a, "smallm full size M=16")
+
+
 @pytest.mark.parametrize("smallm_math", MATHS, indirect=True)
 def test_smallm_group_periods(smallm_math):
     """A plan whose problems are all whole periods (gemm_rows runs it with the
