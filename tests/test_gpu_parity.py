@@ -471,6 +471,25 @@ def test_smallm_group(smallm_math):
     grp.close()
 
 
+@pytest.mark.parametrize("t", ["pn3t", "pn4t"])
+def test_smallm_unaligned_weights(t):
+    """Rows of whole periods whose W is 2-byte but not 16-byte aligned: the
+    DMA kernel needs 16-byte chunks, so the library runs gemm_stream."""
+    n, k, m = 70, WPB[t] * 16, 8
+    w, g = random_matrix(61, t, n, k)
+    X = synth.activation(g, k, m)
+    raw = dev(np.concatenate([np.zeros(2, np.uint8), np.ascontiguousarray(w).reshape(-1)]))
+    wd = raw[2:]
+    assert wd.data_ptr() % 16 == 2
+    Y = torch.full((m, n), 7.0, dtype=torch.float32, device="cuda")
+    say("smallm unaligned W %s" % t)
+    B.pn_gemm_smallm(t, wd, n, k, dev(X), k, m, Y, n)
+    sync()
+    assert B.pn_variant_name(B.pn_last_variant()) == "gemm_stream_mfma"
+    y64, a = pnref.gemm_f64(t, w, n, k, X)
+    assert_gemv_close(Y.cpu().numpy(), y64, a, "smallm unaligned W")
+
+
 @pytest.mark.parametrize("smallm_math", ["mfma", "mfma_stream"], indirect=True)
 @pytest.mark.parametrize("t,n,k", [("pn3t", 17408, 5120), ("pn4t", 5120, 17408)])
 def test_smallm_full_size_m16_sampled(smallm_math, t, n, k):
