@@ -17,10 +17,11 @@
 //
 // Tiles.  A workgroup of eight waves computes 128 rows of X (M) by 256
 // weight rows (N); each wave owns 128 x 32 of it (4 x 1 MFMA tiles), so
-// every weight row is decoded by one wave only.  The K loop takes one block pair (two 34-byte blocks, 68 bytes,
-// 17 aligned dwords: 160 k for pn3t, 128 for pn4t) at a time: the
-// workgroup stages the X tile (128 x 160 or 128 fp16) and the 128 rows'
-// block pairs in LDS with coalesced loads, and each wave decodes its 64
+// every weight row is decoded by one wave only.  The K loop takes one block
+// pair (two 34-byte blocks, 68 bytes, 17 aligned dwords: 160 k for pn3t,
+// 128 for pn4t) at a time: the workgroup stages the X tile (128 x 160 or
+// 128 fp16) and the 256 weight rows' block pairs in LDS by DMA, into one of
+// two stages while the other is computed, and each wave decodes its 32
 // weight rows straight into B operands.
 //
 // Operand layouts (checked on the GPU: lane l of the 32 x 32 x 16 MFMA):
