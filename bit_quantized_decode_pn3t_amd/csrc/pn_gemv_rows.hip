@@ -678,10 +678,17 @@ __global__ __launch_bounds__(kRThreads) void gemv_rows(RArgs a)
     asm volatile("s_waitcnt vmcnt(0)" : "+v"(gv) :: "memory");
     if constexpr (TABLE) {
         // The last wave to finish resets the plan's counters for its next run.
+        // Relaxed ordering is enough: every wave has waited for its own
+        // counter atomics (vmcnt(0) above) before it counts itself done, the
+        // reset depends on the count this atomic returns, and the kernel's end
+        // publishes the reset to the next launch.  (Acquire-release ordering
+        // at agent scope made every wave write back and invalidate its L2 as
+        // it finished: about 100 us per launch of a small plan, 2,048 times
+        // an L2 flush under the waves still streaming.)
         if (lane == 0) {
             const uint32_t nw = gridDim.x * kRWaves;
             uint32_t *done = a.counters + kCounterStride * kPools;
-            if (__hip_atomic_fetch_add(done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == nw - 1) {
+            if (__hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nw - 1) {
                 for (int p = 0; p < kPools; ++p)
                     __hip_atomic_store(a.counters + kCounterStride * p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
