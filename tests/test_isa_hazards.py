@@ -142,3 +142,28 @@ def test_row_tile_kernel_has_no_hazards(tmp_path):
     asm = out.read_text()
     assert asm.count("v_dot2c_f32_f16_dpp") >= 1152  # both kernels, both types
     assert find_hazards(asm) == []
+
+
+KERNEL_SOURCES = ["pn_gemv_rows.hip", "pn_kernels.hip", "pn_smallm.hip", "pn_prefill.hip", "pn_rotate.hip",
+                  "pn_probe.hip"]
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None, reason="no hipcc")
+@pytest.mark.parametrize("src", KERNEL_SOURCES)
+def test_no_cache_maintenance(tmp_path, src):
+    """No kernel writes back or invalidates L2 (buffer_wbl2 / buffer_inv).
+    The compiler emits them for acquire or release atomics at agent scope.
+    The row-tile kernel once counted its finished waves that way, and every
+    finishing wave flushed its XCD's L2 under the waves still streaming.
+    Every atomic here is relaxed: its ordering comes from explicit waits and
+    the kernel boundary."""
+    path = os.path.join(os.path.dirname(SRC), src)
+    out = tmp_path / (src + ".s")
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "--cuda-device-only", "-S",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I" + os.path.join(ROOT, "include"), "-o", str(out), path]
+    subprocess.run(cmd, check=True, capture_output=True, cwd=os.path.dirname(SRC))
+    asm = out.read_text()
+    assert "s_endpgm" in asm
+    bad = [l.strip() for l in asm.splitlines() if re.match(r"\s*buffer_(wbl2|inv)\b", l)]
+    assert bad == [], bad
