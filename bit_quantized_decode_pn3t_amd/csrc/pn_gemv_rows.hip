@@ -515,10 +515,15 @@ template <bool TABLE>
 __global__ __launch_bounds__(kRThreads) void gemv_rows(RArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    __shared__ uint32_t wg_done;  // group launches: waves of this workgroup that have finished
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
     const int gw = blockIdx.x * kRWaves + wave;
     const int g = lane >> 4, r = lane & 15;
+    if constexpr (TABLE) {
+        if (threadIdx.x == 0) wg_done = 0;
+        __syncthreads();
+    }
     uint8_t *ring = lds + wave * kNS * kStage;
 
     Cursor ci;
@@ -678,17 +683,21 @@ __global__ __launch_bounds__(kRThreads) void gemv_rows(RArgs a)
     asm volatile("s_waitcnt vmcnt(0)" : "+v"(gv) :: "memory");
     if constexpr (TABLE) {
         // The last wave to finish resets the plan's counters for its next run.
-        // Relaxed ordering is enough: every wave has waited for its own
-        // counter atomics (vmcnt(0) above) before it counts itself done, the
-        // reset depends on the count this atomic returns, and the kernel's end
-        // publishes the reset to the next launch.  (Acquire-release ordering
-        // at agent scope made every wave write back and invalidate its L2 as
-        // it finished: about 100 us per launch of a small plan, 2,048 times
-        // an L2 flush under the waves still streaming.)
-        if (lane == 0) {
-            const uint32_t nw = gridDim.x * kRWaves;
+        // The waves of a workgroup count themselves in LDS, and the last of
+        // them counts the workgroup in the plan's device counter: 256 device
+        // atomics on that address per launch instead of 2,048.  Relaxed
+        // ordering is enough: every wave has waited for its own counter
+        // atomics (vmcnt(0) above) before it counts itself done, each count
+        // depends on the one before it, the reset depends on the count the
+        // last atomic returns, and the kernel's end publishes the reset to the
+        // next launch.  (Acquire-release ordering at agent scope made every
+        // wave write back and invalidate its L2 as it finished: about 100 us
+        // per launch of a small plan, 2,048 L2 flushes under the waves still
+        // streaming.)
+        if (lane == 0 &&
+            __hip_atomic_fetch_add(&wg_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == kRWaves - 1) {
             uint32_t *done = a.counters + kCounterStride * kPools;
-            if (__hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nw - 1) {
+            if (__hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1) {
                 for (int p = 0; p < kPools; ++p)
                     __hip_atomic_store(a.counters + kCounterStride * p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
