@@ -237,7 +237,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--schedule", default="token", choices=["token", "layer", "gemv", "token_rot"])
-    ap.add_argument("--config", type=int, default=3, choices=[3, 4])
+    ap.add_argument("--config", type=int, default=3, choices=[3, 4],
+                    help="3: the 64-layer sweep at M = 1 (the default); 4: the same sweep with M activation "
+                         "rows per matrix (--m, 8 by default)")
     ap.add_argument("--math", default="mfma", choices=["mfma", "valu"],
                     help="small-batch arithmetic (--config 4)")
     ap.add_argument("--m", type=int, default=8, help="activation rows with --config 4 (1..16)")
