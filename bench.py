@@ -217,7 +217,7 @@ def cpu_baseline(layers, threads, m=None):
     from oracle import pnref
 
     used = pnref.set_threads(threads)
-    recs = synth.sweep_matrices(layers=layers, m=m, config=3 if m is None else 4, threads=threads)
+    recs = synth.sweep_matrices(layers=layers, m=m, config=3 if m is None else 4, threads=min(16, threads))
     sample_bytes = sum(r["W"].nbytes for r in recs)
     pnref.gemv_f64(recs[0]["type"], recs[0]["W"][:64], 64, recs[0]["K"],
                    recs[0]["x"] if m is None else recs[0]["x"][0])  # warm
@@ -229,6 +229,57 @@ def cpu_baseline(layers, threads, m=None):
             pnref.gemm_f64(r["type"], r["W"], r["N"], r["K"], r["x"])
     dt = time.perf_counter() - t0
     return dt, sample_bytes, used
+
+
+def token_timing(B, torch, sw, steps, warmup):
+    """Time the one-launch token schedule of `sw`: HIP events on the launch
+    stream around every launch (one kernel per step), after `warmup` runs."""
+    sw.prepare("token")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        sw.step("token")
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        sw.step("token")
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [a.elapsed_time(b) for a, b in evs], B.pn_variant_name(B.pn_last_variant())
+
+
+def smallm_m8_timing(B, torch, sw, steps, m=8):
+    """The M = 8 verification-batch sweep (the same resident weights, an 8-row
+    activation batch per matrix): one grouped launch per token with the MFMA
+    arithmetic (the library's pick: gemm_rows) and with the VALU arithmetic,
+    each with its kernel's roofline from per-launch events."""
+    v = sw.batch_view(m)
+    bytes_per_token = v.weight_bytes + v.act_bytes
+    out = {"workload": "64-layer 27B-shaped sweep, M=%d, token schedule" % m, "bytes_per_token": bytes_per_token}
+    try:
+        for math in ("mfma", "valu"):
+            B.pn_set_smallm_math(math)
+            v.close()  # a plan keeps the arithmetic it was created with
+            wall, ev_ms, variant = token_timing(B, torch, v, steps, 5)
+            kern_ms = sum(ev_ms) / len(ev_ms)
+            achieved = bytes_per_token / (kern_ms * 1e-3) / 1e9
+            workload = "sweep64_m%d_token_%s" % (m, math)
+            out[math] = {"ms_per_token": round(wall / steps * 1e3, 4), "tokens_per_s": round(steps / wall, 2),
+                         "gbps": round(bytes_per_token / (wall / steps) / 1e9, 1), "variant": variant,
+                         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS,
+                                      "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),
+                                      "traffic": measured_traffic(workload, "smallm"),
+                                      "kernel": variant.replace("_group", ""), "kernel_avg_ms": round(kern_ms, 4),
+                                      "algorithmic_bytes_per_launch": bytes_per_token}}
+            log("M=%d token %s: %.4f ms per token (%s)" % (m, math, kern_ms, variant))
+    finally:
+        B.pn_set_smallm_math("mfma")
+        v.close()
+        del v
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -283,7 +334,8 @@ def main():
         sys.exit(2)
     if m is not None:
         B.pn_set_smallm_math(args.math)
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))  # input generation
+    cpu_threads = len(os.sched_getaffinity(0))  # the oracle: every core of the affinity mask
 
     t0 = time.perf_counter()
     log("generating %d layers (M=%s) with %d threads" % (args.layers, m or 1, threads))
@@ -373,6 +425,10 @@ def main():
             log("schedule %s: %.1f tok/s" % (key, args.steps / w2))
         if m is not None:
             B.pn_set_smallm_math(args.math)
+    smallm = None
+    if m is None and not args.no_secondary:
+        log("M=8 verification-batch sweep on the same weights")
+        smallm = smallm_m8_timing(B, torch, sw, args.steps)
     sw.close()
     del sw
     torch.cuda.empty_cache()
@@ -406,17 +462,24 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu_layers = args.cpu_layers or (64 if m is None else 8)
-        log("cpu baseline: oracle on %d layers, %d threads" % (cpu_layers, threads))
-        dt, sample_bytes, used = cpu_baseline(cpu_layers, threads, m)
+        log("cpu baseline: oracle on %d layers, %d threads" % (cpu_layers, cpu_threads))
+        dt, sample_bytes, used = cpu_baseline(cpu_layers, cpu_threads, m)
         weights_per_token = sum(synth.row_bytes(t, k) * n for _, t, n, k in synth.SWEEP_LAYER) * args.layers
         token_fraction = sample_bytes / weights_per_token
         cpu = {"value": round(token_fraction / dt, 4), "unit": "tok/s", "cores": used, "kind": "oracle",
                "sample": "first %d of %d layers (%.2f GB packed, %.1f%% of a token) in %.2f s; "
-                         "fp64 decode+%s, OpenMP over rows" % (cpu_layers, args.layers, sample_bytes / 1e9,
-                                                              100 * token_fraction, dt,
-                                                              "GEMV" if m is None else "GEMM (M=%d)" % m),
+                         "fp64 decode+%s, OpenMP over rows on every core of the affinity mask"
+                         % (cpu_layers, args.layers, sample_bytes / 1e9, 100 * token_fraction, dt,
+                            "GEMV" if m is None else "GEMM (M=%d)" % m),
                "gbps_packed": round(sample_bytes / dt / 1e9, 3),
-               "cpu_model": cpu_model(), "host_read_gbps": host_read_gbps()}
+               "affinity_cores": cpu_threads, "cpu_model": cpu_model(), "host_read_gbps": host_read_gbps()}
+        if m is None and not args.no_secondary:
+            m8_layers = 8
+            log("cpu baseline: oracle at M=8 on %d layers" % m8_layers)
+            dt8, bytes8, used8 = cpu_baseline(m8_layers, cpu_threads, 8)
+            cpu["m8"] = {"value": round(bytes8 / weights_per_token / dt8, 4), "unit": "tok/s", "cores": used8,
+                         "sample": "first %d layers (%.2f GB packed) at M=8 in %.2f s; the oracle decodes each "
+                                   "row once per activation row" % (m8_layers, bytes8 / 1e9, dt8)}
         one_layers = max(1, cpu_layers // 8)
         dt1, bytes1, _ = cpu_baseline(one_layers, 1, m)
         cpu["one_thread"] = {"value": round(bytes1 / weights_per_token / dt1, 4), "unit": "tok/s",
@@ -449,6 +512,7 @@ def main():
         "other_schedules": secondary,
         "per_config": per_config,
         "prefill": prefill,
+        "smallm_m8": smallm,
         "kernel_hash": kernel_hash(kind),
     }
     print(json.dumps(out), flush=True)

@@ -709,8 +709,6 @@ __global__ __launch_bounds__(kRThreads) void gemv_rows(RArgs a)
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-int g_kernel = PN_GEMV_AUTO;
-
 void rfill(RProb &p, int t, const void *W, int64_t N, int64_t K, const void *x, float *y)
 {
     memset(&p, 0, sizeof(p));
@@ -729,21 +727,15 @@ int rows_waves() { return device_cus() * kRWaves; }
 
 bool set_rows_attr()
 {
-    static int done = 0;  // per process; the attribute is per function
-    if (!done) {
-        if (hipFuncSetAttribute((const void *)gemv_rows<true>, hipFuncAttributeMaxDynamicSharedMemorySize, kRing) !=
-                hipSuccess ||
-            hipFuncSetAttribute((const void *)gemv_rows<false>, hipFuncAttributeMaxDynamicSharedMemorySize, kRing) !=
-                hipSuccess)
-            return false;
-        done = 1;
-    }
-    return true;
+    return hipFuncSetAttribute((const void *)gemv_rows<true>, hipFuncAttributeMaxDynamicSharedMemorySize, kRing) ==
+               hipSuccess &&
+           hipFuncSetAttribute((const void *)gemv_rows<false>, hipFuncAttributeMaxDynamicSharedMemorySize, kRing) ==
+               hipSuccess;
 }
 
 pn_status rlaunch(const RArgs &a, hipStream_t s, int variant)
 {
-    if (!set_rows_attr()) return PN_ELAUNCH;
+    if (!once_per_device(kAttrRows, set_rows_attr)) return PN_ELAUNCH;
     if (a.table)
         hipLaunchKernelGGL(gemv_rows<true>, dim3((unsigned)device_cus()), dim3(kRThreads), kRing, s, a);
     else
@@ -760,7 +752,7 @@ pn_status rlaunch(const RArgs &a, hipStream_t s, int variant)
 // offsets fit the kernel's 32-bit arithmetic.
 bool pn::host::rows_ok(int t, const void *W, int64_t K, const void *x)
 {
-    if (pn_get_gemv_kernel() == PN_GEMV_STREAM) return false;
+    if (gemv_kernel_choice() == PN_GEMV_STREAM) return false;
     if (((uintptr_t)W & 15) != 0 || ((uintptr_t)x & 15) != 0) return false;
     const int64_t nb = K / wpb(t);
     if (nb % 8 != 0) return false;
@@ -770,7 +762,7 @@ bool pn::host::rows_ok(int t, const void *W, int64_t K, const void *x)
 // Is a launch of `tiles` 16-row tiles large enough for gemv_rows?
 bool pn::host::rows_pays(int64_t tiles)
 {
-    if (pn_get_gemv_kernel() == PN_GEMV_ROWS) return true;
+    if (gemv_kernel_choice() == PN_GEMV_ROWS) return true;
     return tiles >= (int64_t)kMinTilesPerCu * device_cus();
 }
 
@@ -838,6 +830,11 @@ pn_status pn::host::rows_group_create(const pn_gemv_desc *descs, int count, pn_g
             if (host[i].nwin == w)
                 for (int t = 0; t < host[i].tiles; ++t) lut[k++] = ((uint32_t)i << 20) | (uint32_t)t;
     free(host);
+    if (current_device() < 0) {
+        free(blob);
+        free(g);
+        return PN_EUNSUPPORTED;
+    }
     if (hipMalloc(&g->table, coff + cbytes) != hipSuccess) {
         free(blob);
         free(g);
@@ -851,6 +848,7 @@ pn_status pn::host::rows_group_create(const pn_gemv_desc *descs, int count, pn_g
     }
     free(blob);
     g->kind = kGroupGemvRows;
+    g->device = current_device();
     g->count = count;
     g->total_tiles = (int)total;
     g->lds = kRing;
@@ -870,16 +868,3 @@ pn_status pn::host::rows_group_run(const pn_group *g, hipStream_t s)
     a.total_tiles = g->total_tiles;
     return rlaunch(a, s, kVarGroupRows);
 }
-
-extern "C" {
-
-pn_status pn_set_gemv_kernel(pn_gemv_kernel k)
-{
-    if (k != PN_GEMV_AUTO && k != PN_GEMV_STREAM && k != PN_GEMV_ROWS) return PN_EINVAL;
-    __atomic_store_n(&g_kernel, (int)k, __ATOMIC_RELAXED);
-    return PN_OK;
-}
-
-pn_gemv_kernel pn_get_gemv_kernel(void) { return (pn_gemv_kernel)__atomic_load_n(&g_kernel, __ATOMIC_RELAXED); }
-
-}  // extern "C"

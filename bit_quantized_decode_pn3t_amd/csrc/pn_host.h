@@ -46,8 +46,26 @@ inline pn_status check_matrix(int t, const void *W, int64_t N, int64_t K)
     return PN_OK;
 }
 
-// Compute units of the current device (256 if the query fails).
+// Devices the library keeps per-device facts for (ordinals 0..kMaxDevices-1;
+// a call made with a higher ordinal current returns PN_EUNSUPPORTED).
+constexpr int kMaxDevices = 64;
+
+// Ordinal of the current device, or -1 if it cannot be used here.
+int current_device();
+
+// Compute units of the current device (256 if the query fails).  Filled once
+// per device, thread-safe.
 int device_cus();
+
+// Run `set` (raising a kernel's LDS limit with hipFuncSetAttribute) once per
+// device and flag; later calls return the first call's result.  Thread-safe.
+enum AttrFlag { kAttrRows = 0, kAttrSmallM = 1, kAttrPrefill = 2, kAttrProbe = 3, kAttrCount = 4 };
+bool once_per_device(AttrFlag f, bool (*set)());
+
+// The calling thread's kernel selections (pn_set_gemv_kernel and
+// pn_set_smallm_math act on the calling host thread only).
+int gemv_kernel_choice();
+int smallm_math_choice();
 
 enum GroupKind { kGroupGemv = 0, kGroupSmallM = 1, kGroupGemvRows = 2 };
 
@@ -64,6 +82,7 @@ struct pn_group {
     int flags;          // kind-specific launch choice
     void *rot;          // problems with rotated inputs: RotJob list, then the rotated copies
     int rot_jobs;       // 1024-element blocks to rotate before the GEMV launch (0: none)
+    int device;         // device current at creation: the plan's memory lives there
 };
 
 namespace pn {

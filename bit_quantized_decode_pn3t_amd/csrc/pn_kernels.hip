@@ -20,6 +20,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "pn_device.h"
 #include "pn_host.h"
 
@@ -399,32 +402,64 @@ __global__ __launch_bounds__(256) void dequant(const uint8_t *W, int64_t N, int6
 constexpr int kR = PN_ROWS_PER_GROUP;   // rows per group in gemv_stream
 constexpr int kU = PN_ITEMS_IN_FLIGHT;  // items (one pass of 8 blocks x R rows) in flight per wave
 
-// Per device: CU count and gemv_stream occupancy by LDS size (1 KiB steps).
+// Per device: CU count (filled once, under a once flag) and gemv_stream
+// occupancy by LDS size in 1 KiB steps (0 = not queried yet; concurrent
+// queries of one entry compute and store the same value).
 struct DeviceInfo {
     int cus = 0;
-    signed char occ[65];
+    std::atomic<signed char> occ[65];
 };
 
-DeviceInfo g_dev[64];
+DeviceInfo g_dev[kMaxDevices];
+std::once_flag g_dev_once[kMaxDevices];
 
 const DeviceInfo &device_info()
 {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
     DeviceInfo &d = g_dev[dev];
-    if (d.cus == 0) {
+    std::call_once(g_dev_once[dev], [&d, dev]() {
         int cus = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
-        memset(d.occ, 0, sizeof(d.occ));
+        for (auto &o : d.occ) o.store(0, std::memory_order_relaxed);
         d.cus = cus;
-    }
+    });
     return d;
 }
 
 }  // namespace
 
 int pn::host::device_cus() { return device_info().cus; }
+
+int pn::host::current_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+    return dev;
+}
+
+namespace {
+struct AttrOnce {
+    std::once_flag once;
+    bool ok = false;
+};
+AttrOnce g_attr[kMaxDevices][kAttrCount];
+thread_local int t_gemv_kernel = PN_GEMV_AUTO;
+thread_local int t_smallm_math = PN_SMALLM_MFMA;
+}  // namespace
+
+bool pn::host::once_per_device(AttrFlag f, bool (*set)())
+{
+    const int dev = current_device();
+    if (dev < 0) return false;
+    AttrOnce &a = g_attr[dev][f];
+    std::call_once(a.once, [&a, set]() { a.ok = set(); });
+    return a.ok;
+}
+
+int pn::host::gemv_kernel_choice() { return t_gemv_kernel; }
+int pn::host::smallm_math_choice() { return t_smallm_math; }
 
 namespace {
 
@@ -433,15 +468,17 @@ int stream_wgs_per_cu(const DeviceInfo &dc, int lds)
     DeviceInfo &d = const_cast<DeviceInfo &>(dc);
     int q = (lds + 1023) / 1024;
     q = q < 0 ? 0 : (q > 64 ? 64 : q);
-    if (d.occ[q] == 0) {
+    signed char o = d.occ[q].load(std::memory_order_relaxed);
+    if (o == 0) {
         int occ = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemv_stream<kR, kU, 2>, kThreads,
                                                          (size_t)q * 1024) != hipSuccess ||
             occ <= 0)
             occ = 1;
-        d.occ[q] = (signed char)(occ > 127 ? 127 : occ);
+        o = (signed char)(occ > 127 ? 127 : occ);
+        d.occ[q].store(o, std::memory_order_relaxed);
     }
-    return d.occ[q];
+    return o;
 }
 
 Prob make_prob(int t, const void *W, int64_t N, int64_t K, const void *x, float *y)
@@ -673,6 +710,11 @@ pn_status group_create_plain(const pn_gemv_desc *descs, int count, pn_group **ou
         free(host);
         return PN_ENOMEM;
     }
+    if (current_device() < 0) {
+        free(host);
+        free(g);
+        return PN_EUNSUPPORTED;
+    }
     if (hipMalloc(&g->table, sizeof(Prob) * (size_t)count) != hipSuccess) {
         free(host);
         free(g);
@@ -686,6 +728,7 @@ pn_status group_create_plain(const pn_gemv_desc *descs, int count, pn_group **ou
     }
     free(host);
     g->kind = kGroupGemv;
+    g->device = current_device();
     g->count = count;
     g->total_tiles = (int)tiles;
     g->lds = lds;
@@ -759,6 +802,7 @@ pn_status pn_group_create(const pn_gemv_desc *descs, int count, pn_group **out)
 pn_status pn_group_run(const pn_group *g, void *stream)
 {
     if (!g) return PN_EINVAL;
+    if (current_device() != g->device) return PN_EUNSUPPORTED;  // the plan's tables live on its device
     if (g->rot_jobs > 0) {
         const pn_status st = rotate_jobs_launch((const RotJob *)g->rot, g->rot_jobs, (hipStream_t)stream);
         if (st != PN_OK) return st;
@@ -797,6 +841,24 @@ const char *pn_status_str(pn_status e)
 }
 
 int pn_last_variant(void) { return g_last_variant; }
+
+pn_status pn_set_gemv_kernel(pn_gemv_kernel k)
+{
+    if (k != PN_GEMV_AUTO && k != PN_GEMV_STREAM && k != PN_GEMV_ROWS) return PN_EINVAL;
+    t_gemv_kernel = (int)k;
+    return PN_OK;
+}
+
+pn_gemv_kernel pn_get_gemv_kernel(void) { return (pn_gemv_kernel)t_gemv_kernel; }
+
+pn_status pn_set_smallm_math(pn_smallm_math m)
+{
+    if (m != PN_SMALLM_MFMA && m != PN_SMALLM_VALU) return PN_EINVAL;
+    t_smallm_math = (int)m;
+    return PN_OK;
+}
+
+pn_smallm_math pn_get_smallm_math(void) { return (pn_smallm_math)t_smallm_math; }
 
 const char *pn_variant_name(int v)
 {

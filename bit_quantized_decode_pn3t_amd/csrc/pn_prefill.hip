@@ -282,16 +282,10 @@ __global__ __launch_bounds__(256) void zero_rows(float *Y, int64_t ldy, int32_t 
 
 bool set_prefill_attr()
 {
-    static int done = 0;
-    if (!done) {
-        if (hipFuncSetAttribute((const void *)gemm_prefill<0>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                Pf<0>::LDS) != hipSuccess ||
-            hipFuncSetAttribute((const void *)gemm_prefill<1>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                Pf<1>::LDS) != hipSuccess)
-            return false;
-        done = 1;
-    }
-    return true;
+    return hipFuncSetAttribute((const void *)gemm_prefill<0>, hipFuncAttributeMaxDynamicSharedMemorySize, Pf<0>::LDS) ==
+               hipSuccess &&
+           hipFuncSetAttribute((const void *)gemm_prefill<1>, hipFuncAttributeMaxDynamicSharedMemorySize, Pf<1>::LDS) ==
+               hipSuccess;
 }
 
 }  // namespace
@@ -309,7 +303,8 @@ pn_status pn_gemm_prefill(pn_type t, const void *W, int64_t N, int64_t K, const 
     if (M > INT32_MAX - kPfM || (M + kPfM - 1) / kPfM > 65535) return PN_EUNSUPPORTED;
     if ((uint64_t)kPfM * (uint64_t)ldx * 2u >= 0x80000000ull) return PN_EUNSUPPORTED;  // 32-bit tile offsets
     if (N * M > ((int64_t)1 << 40)) return PN_EUNSUPPORTED;
-    if (!set_prefill_attr()) return PN_ELAUNCH;
+    if ((uint64_t)kPfN * (uint64_t)nb * 34u >= 0x80000000ull) return PN_EUNSUPPORTED;  // 32-bit row offsets
+    if (!once_per_device(kAttrPrefill, set_prefill_attr)) return PN_ELAUNCH;
     PfArgs a;
     a.W = (const uint8_t *)W;
     a.X = X;

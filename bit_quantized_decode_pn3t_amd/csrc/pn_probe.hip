@@ -15,6 +15,7 @@
 #include <stdint.h>
 
 #include "../../include/pn.h"
+#include "pn_host.h"
 
 namespace {
 
@@ -69,6 +70,12 @@ __global__ __launch_bounds__(kProbeThreads) void read_probe(const uint8_t *buf, 
     out[gw * 64 + lane] = acc;
 }
 
+bool set_probe_attr()
+{
+    return hipFuncSetAttribute((const void *)read_probe, hipFuncAttributeMaxDynamicSharedMemorySize, kProbeLds) ==
+           hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -97,13 +104,7 @@ pn_status pn_read_probe(const void *buf, size_t bytes, void *scratch, size_t scr
     uint64_t span = bytes / waves;
     span -= span % kProbeStage;
     if (span < kProbeStage || span > 0x7fffffffu) return PN_ESHAPE;
-    static int attr = 0;
-    if (!attr) {
-        if (hipFuncSetAttribute((const void *)read_probe, hipFuncAttributeMaxDynamicSharedMemorySize, kProbeLds) !=
-            hipSuccess)
-            return PN_ELAUNCH;
-        attr = 1;
-    }
+    if (!pn::host::once_per_device(pn::host::kAttrProbe, set_probe_attr)) return PN_ELAUNCH;
     hipLaunchKernelGGL(read_probe, dim3((unsigned)grid), dim3(kProbeThreads), kProbeLds, (hipStream_t)stream,
                        (const uint8_t *)buf, (uint32_t)span, (uint32_t *)scratch);
     if (hipGetLastError() != hipSuccess) return PN_ELAUNCH;

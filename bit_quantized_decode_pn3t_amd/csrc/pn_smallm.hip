@@ -36,6 +36,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include <type_traits>
 
 #include "pn_device.h"
@@ -723,32 +725,33 @@ __global__ __launch_bounds__(kDmThreads) void gemm_rows(SmArgs args)
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-int g_math = PN_SMALLM_MFMA;  // process-wide choice of pn_set_smallm_math
-
+// Per device: workgroups per CU by arithmetic and LDS KiB (0 = not queried
+// yet; concurrent queries of one entry compute and store the same value).
 struct SmDevice {
-    int ready = 0;
-    signed char occ[2][161];  // workgroups per CU by math and LDS KiB (0 = not queried)
+    std::atomic<signed char> occ[2][161];
 };
-SmDevice g_sm[64];
+SmDevice g_sm[kMaxDevices];
+
+// Activation chunks above 64 KiB need the kernels' LDS limit raised (once
+// per device).
+bool set_smallm_attr()
+{
+    return hipFuncSetAttribute((const void *)gemm_stream<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               kSmLdsMax) == hipSuccess &&
+           hipFuncSetAttribute((const void *)gemm_stream<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               kSmLdsMax) == hipSuccess &&
+           hipFuncSetAttribute((const void *)gemm_rows, hipFuncAttributeMaxDynamicSharedMemorySize, kSmLdsMax) ==
+               hipSuccess;
+}
 
 int sm_wgs_per_cu(bool mfma, int lds)
 {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    const int dev = current_device() < 0 ? 0 : current_device();
     SmDevice &d = g_sm[dev];
-    if (!d.ready) {
-        memset(d.occ, 0, sizeof(d.occ));
-        // activation chunks above 64 KiB need the kernels' LDS limit raised
-        (void)hipFuncSetAttribute((const void *)gemm_stream<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  kSmLdsMax);
-        (void)hipFuncSetAttribute((const void *)gemm_stream<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  kSmLdsMax);
-        (void)hipFuncSetAttribute((const void *)gemm_rows, hipFuncAttributeMaxDynamicSharedMemorySize, kSmLdsMax);
-        d.ready = 1;
-    }
     int q = (lds + 1023) / 1024;
     q = q < 0 ? 0 : (q > 160 ? 160 : q);
-    signed char &o = d.occ[mfma ? 1 : 0][q];
+    std::atomic<signed char> &slot = d.occ[mfma ? 1 : 0][q];
+    signed char o = slot.load(std::memory_order_relaxed);
     if (o == 0) {
         int occ = 0;
         const hipError_t e = mfma ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_stream<true>, kSmThreads,
@@ -757,6 +760,7 @@ int sm_wgs_per_cu(bool mfma, int lds)
                                                                                   (size_t)q * 1024);
         if (e != hipSuccess || occ <= 0) occ = 1;
         o = (signed char)(occ > 127 ? 127 : occ);
+        slot.store(o, std::memory_order_relaxed);
     }
     return o;
 }
@@ -767,7 +771,7 @@ int sm_wgs_per_cu(bool mfma, int lds)
 // allows it (pn_set_gemv_kernel: anything but PN_GEMV_STREAM).
 bool sm_dma_ok(int t, const void *W, int64_t K, bool mfma)
 {
-    if (!mfma || pn_get_gemv_kernel() == PN_GEMV_STREAM) return false;
+    if (!mfma || gemv_kernel_choice() == PN_GEMV_STREAM) return false;
     if (((uintptr_t)W & 15) != 0) return false;
     const int64_t nb = K / wpb(t);
     return nb % 8 == 0 && nb * 34 * kDmRows <= INT32_MAX;
@@ -819,13 +823,13 @@ int sm_lds(const SmProb &p) { return p.M * p.stride; }
 
 pn_status sm_launch(const SmArgs &a, int lds, bool mfma, bool dma, hipStream_t s, int variant)
 {
+    if (!once_per_device(kAttrSmallM, set_smallm_attr)) return PN_ELAUNCH;
     int grid = device_cus() * (dma ? 1 : sm_wgs_per_cu(mfma, lds));  // gemm_rows takes the whole LDS
     if (grid > a.total_tiles) grid = a.total_tiles;
     if (grid < 1) grid = 1;
-    if (dma) {
-        (void)sm_wgs_per_cu(true, lds);  // raises the kernels' LDS limit once per device
+    if (dma)
         hipLaunchKernelGGL(gemm_rows, dim3(grid), dim3(kDmThreads), kSmLdsMax, s, a);
-    } else if (mfma)
+    else if (mfma)
         hipLaunchKernelGGL(gemm_stream<true>, dim3(grid), dim3(kSmThreads), lds, s, a);
     else
         hipLaunchKernelGGL(gemm_stream<false>, dim3(grid), dim3(kSmThreads), lds, s, a);
@@ -851,21 +855,12 @@ pn_status pn::host::smallm_group_run(const pn_group *g, hipStream_t s)
 
 extern "C" {
 
-pn_status pn_set_smallm_math(pn_smallm_math m)
-{
-    if (m != PN_SMALLM_MFMA && m != PN_SMALLM_VALU) return PN_EINVAL;
-    __atomic_store_n(&g_math, (int)m, __ATOMIC_RELAXED);
-    return PN_OK;
-}
-
-pn_smallm_math pn_get_smallm_math(void) { return (pn_smallm_math)__atomic_load_n(&g_math, __ATOMIC_RELAXED); }
-
 pn_status pn_gemm_smallm(pn_type t, const void *W, int64_t N, int64_t K, const void *X, int64_t ldx, int M,
                          float *Y, int64_t ldy, void *stream)
 {
     SmArgs a;
     memset(&a, 0, sizeof(a));
-    const bool mfma = pn_get_smallm_math() == PN_SMALLM_MFMA;
+    const bool mfma = smallm_math_choice() == PN_SMALLM_MFMA;
     const bool dma = type_ok(t) && W && K >= wpb(t) && sm_dma_ok(t, W, K, mfma);
     pn_status st = sm_make(t, W, N, K, X, ldx, M, Y, ldy, mfma, dma, a.p0);
     if (st) return st;
@@ -885,7 +880,7 @@ pn_status pn_group_create_smallm(const pn_gemm_desc *descs, int count, pn_group 
     int lds = 0;
     int64_t tiles = 0;
     pn_status st = PN_OK;
-    const int math = pn_get_smallm_math();
+    const int math = smallm_math_choice();
     // gemm_rows runs the plan if it takes every problem (one launch, one kernel)
     bool dma = true;
     for (int i = 0; i < count && dma; ++i) {
@@ -911,6 +906,11 @@ pn_status pn_group_create_smallm(const pn_gemm_desc *descs, int count, pn_group 
         free(host);
         return PN_ENOMEM;
     }
+    if (current_device() < 0) {
+        free(host);
+        free(g);
+        return PN_EUNSUPPORTED;
+    }
     if (hipMalloc(&g->table, sizeof(SmProb) * (size_t)count) != hipSuccess) {
         free(host);
         free(g);
@@ -924,6 +924,7 @@ pn_status pn_group_create_smallm(const pn_gemm_desc *descs, int count, pn_group 
     }
     free(host);
     g->kind = kGroupSmallM;
+    g->device = current_device();
     g->count = count;
     g->total_tiles = (int)tiles;
     g->lds = lds;

@@ -27,9 +27,10 @@ LAYER_GROUPS = ((0, 1, 2), (3,), (4, 5), (6,))
 
 class Sweep:
     def __init__(self, layers=synth.SWEEP_LAYERS, m=None, device="cuda", threads=16,
-                 sample=None):
+                 sample=None, unused_bits=False):
         """Generate and upload the sweep.  `sample(rec)` (optional) sees each
-        matrix on the host before it is dropped, e.g. to keep some rows."""
+        matrix on the host before it is dropped, e.g. to keep some rows.
+        `unused_bits`: pn3t words keep random bits 15 and 31."""
         self.layers = layers
         self.m = m
         self.device = torch.device(device)
@@ -50,9 +51,25 @@ class Sweep:
             self.act_bytes += x.numel() * 2 + y.numel() * 4
 
         synth.sweep_matrices(layers=layers, m=m, config=3 if m is None else 4, threads=threads,
-                             consume=consume)
+                             consume=consume, unused_bits=unused_bits)
         self.groups = {}
         self.graph = None
+
+    def batch_view(self, m):
+        """The same resident weights with an M-row activation batch per matrix
+        (drawn from config 4's streams, as a Sweep(m=m) would) and its own
+        outputs: the M = 8 workload without a second copy of the weights."""
+        v = Sweep.__new__(Sweep)
+        v.layers, v.m, v.device = self.layers, m, self.device
+        v.mats, v.weight_bytes, v.act_bytes = [], self.weight_bytes, 0
+        for e in self.mats:
+            n, k = e["N"], e["K"]
+            x = torch.from_numpy(synth.activation(synth.rng(4, e["layer"], e["mat"]), k, m)).to(self.device)
+            y = torch.empty((m, n), dtype=torch.float32, device=self.device)
+            v.mats.append(dict(e, x=x, y=y))
+            v.act_bytes += x.numel() * 2 + y.numel() * 4
+        v.groups, v.graph = {}, None
+        return v
 
     # -- schedules --------------------------------------------------------
     def _problem(self, e):

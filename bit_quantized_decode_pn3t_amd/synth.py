@@ -108,12 +108,14 @@ def config2_weights():
     return wg, wu, x
 
 
-def sweep_matrix(layer, mat, with_x=True, m=None, config=3):
+def sweep_matrix(layer, mat, with_x=True, m=None, config=3, unused_bits=False):
     """One matrix of the sweep: weights from config 3's stream (config 4 reuses
-    them) and an activation (or an [m, K] batch) from `config`'s stream."""
+    them) and an activation (or an [m, K] batch) from `config`'s stream.
+    With `unused_bits`, pn3t words keep random bits 15 and 31 (readers must
+    ignore them); the codes are the same either way."""
     name, t, n, k = SWEEP_LAYER[mat]
     g = rng(3, layer, mat)
-    w = random_blocks(g, t, n, k)
+    w = random_blocks(g, t, n, k, unused_bits=unused_bits)
     out = dict(name=name, type=t, N=n, K=k, W=w)
     if with_x:
         if m is None and config == 3:
@@ -123,7 +125,7 @@ def sweep_matrix(layer, mat, with_x=True, m=None, config=3):
     return out
 
 
-def sweep_matrices(layers=SWEEP_LAYERS, m=None, config=3, threads=8, consume=None):
+def sweep_matrices(layers=SWEEP_LAYERS, m=None, config=3, threads=8, consume=None, unused_bits=False):
     """Generate every (layer, matrix) of the sweep with a thread pool (numpy's
     generators release the GIL).  With `consume`, each result is handed to it
     (in layer/matrix order) and dropped, so the host never holds the whole set."""
@@ -133,12 +135,12 @@ def sweep_matrices(layers=SWEEP_LAYERS, m=None, config=3, threads=8, consume=Non
     with _cf.ThreadPoolExecutor(max_workers=threads) as ex:
         futs = {}
         for i in range(min(window, len(jobs))):
-            futs[i] = ex.submit(sweep_matrix, jobs[i][0], jobs[i][1], True, m, config)
+            futs[i] = ex.submit(sweep_matrix, jobs[i][0], jobs[i][1], True, m, config, unused_bits)
         for i, (l, j) in enumerate(jobs):
             r = futs.pop(i).result()
             nxt = i + window
             if nxt < len(jobs):
-                futs[nxt] = ex.submit(sweep_matrix, jobs[nxt][0], jobs[nxt][1], True, m, config)
+                futs[nxt] = ex.submit(sweep_matrix, jobs[nxt][0], jobs[nxt][1], True, m, config, unused_bits)
             r["layer"], r["mat"] = l, j
             if consume is not None:
                 consume(r)

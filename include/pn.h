@@ -5,7 +5,7 @@
  *   - "Every block is 34 bytes": an fp16 scale d (2 bytes) followed by eight
  *     32-bit code words.  pn3t packs ten 3-bit codes per word (80 weights per
  *     block); pn4t packs eight 4-bit codes per word (64 weights per block).
- *     "A row must hold a whole number of blocks": K is a multiple of 80 or 64.
+ *     A row is made of whole blocks, so K is a multiple of 80 or 64.
  *   - "Codes never straddle the two halves of a word": even codes sit in the
  *     low 16 bits, odd codes in the high 16 bits, at the same offsets.
  *   - "Exact decode in fp32": weight = d * (n - z), exact in binary32.
@@ -26,8 +26,18 @@
  * Streams: `stream` is a hipStream_t (NULL = the default stream).  Calls
  * enqueue work and return without synchronising; device faults surface at
  * the caller's next synchronisation.  The calls allocate nothing (except
- * pn_group_create, documented there) and are safe to call from several host
- * threads at once.
+ * the group-create calls, documented there).
+ *
+ * Threads: the calls may be made from several host threads at once, with
+ * two exceptions.  A group plan must not run concurrently with itself (two
+ * runs of one plan on different streams, or graph launches of it that
+ * overlap): some plans keep tile counters in the plan's device memory, and
+ * two runs sharing them would each compute only part of the output.  And a
+ * plan must not be destroyed while another thread runs it.  The kernel
+ * selections (pn_set_gemv_kernel, pn_set_smallm_math) belong to the calling
+ * host thread, and the variant census (pn_last_variant) too.  Per-device
+ * facts the library caches (compute-unit count, occupancy, raised LDS
+ * limits) are filled once, under a lock.
  *
  * Errors: arguments are checked on the host before any launch; a failing
  * check returns a negative pn_status and enqueues nothing.
@@ -122,8 +132,9 @@ pn_status pn_gemm_prefill(pn_type t, const void *W, int64_t N, int64_t K,
  *                   64-layer token);
  *   PN_SMALLM_VALU  per-lane fp16 dot products (v_dot2_f32_f16) reduced
  *                   across the lanes of a row.
- * The setting is process-wide and read when a call is made or a group is
- * created (a group keeps the choice it was created with).  Returns PN_EINVAL
+ * The setting belongs to the calling host thread (every thread starts with
+ * PN_SMALLM_MFMA) and is read when that thread makes a call or creates a
+ * group (a group keeps the choice it was created with).  Returns PN_EINVAL
  * for an unknown value. */
 typedef enum { PN_SMALLM_MFMA = 0, PN_SMALLM_VALU = 1 } pn_smallm_math;
 pn_status pn_set_smallm_math(pn_smallm_math m);
@@ -142,8 +153,10 @@ pn_smallm_math pn_get_smallm_math(void);
  *   PN_GEMV_STREAM  always the register-pipeline kernel;
  *   PN_GEMV_ROWS    the row-tile kernel wherever it applies, whatever the
  *                   launch size.
- * All meet the same accuracy bar.  Process-wide; read when a call is made or
- * a group is created.  Returns PN_EINVAL for an unknown value. */
+ * All meet the same accuracy bar.  The setting belongs to the calling host
+ * thread (every thread starts with PN_GEMV_AUTO) and is read when that
+ * thread makes a call or creates a group.  Returns PN_EINVAL for an unknown
+ * value. */
 typedef enum { PN_GEMV_AUTO = 0, PN_GEMV_STREAM = 1, PN_GEMV_ROWS = 2 } pn_gemv_kernel;
 pn_status pn_set_gemv_kernel(pn_gemv_kernel k);
 pn_gemv_kernel pn_get_gemv_kernel(void);
@@ -204,8 +217,10 @@ typedef struct pn_group pn_group;
  * whole groups of 8 blocks (K a multiple of 640 for pn3t, 512 for pn4t) with
  * 2*K <= 64 KiB of activation, and other shapes return PN_EUNSUPPORTED
  * (pn_gemv takes them one at a time).  The kernel choice is made here, once,
- * for the device current at this call; running the plan on a device with a
- * different number of compute units returns PN_EUNSUPPORTED. */
+ * for the device current at this call, and the plan's tables are placed in
+ * that device's memory: pn_group_run returns PN_EUNSUPPORTED when another
+ * device is current.  A plan must not run concurrently with itself (see
+ * "Threads" above). */
 pn_status pn_group_create(const pn_gemv_desc *descs, int count, pn_group **out);
 
 /* The small-batch counterpart: each entry is one pn_gemm_smallm problem
@@ -225,7 +240,12 @@ typedef struct pn_gemm_desc {
 
 pn_status pn_group_create_smallm(const pn_gemm_desc *descs, int count, pn_group **out);
 
-/* Enqueue all problems of a plan (either kind) as one launch on `stream`. */
+/* Enqueue all problems of a plan (either kind) as one launch on `stream`
+ * (plus the rotation launch ahead of it for PN_DESC_ROTATE entries).  Runs
+ * of one plan must be ordered (one stream, or waits between streams): a run
+ * resets the plan's tile counters as its last wave finishes, ready for the
+ * next run.  PN_EUNSUPPORTED if the device current at this call is not the
+ * plan's. */
 pn_status pn_group_run(const pn_group *g, void *stream);
 
 /* Free a plan (NULL is allowed).  Synchronises the device first. */

@@ -131,6 +131,11 @@ def test_prefill_host_checks():
     assert call(X=X16 + 8) == PN_EALIGN
     assert call(ldx=644) == PN_EALIGN
     assert call(Y=FAKE + 2) == PN_EALIGN
+    # rows whose 256-row tile spans 2 GiB or more would overflow the kernel's
+    # 32-bit offsets: refused before any launch, never wrapped
+    big = 80 * 2 * 126_400  # pn3t, an even number of blocks, 256 rows x 8.6 MB
+    assert call(K=big, ldx=big) == -4
+    assert call(t=1, K=64 * 2 * 126_400, ldx=64 * 2 * 126_400) == -4
 
 
 def test_rotate_host_checks():
@@ -173,23 +178,45 @@ def test_smallm_group_host_checks():
     assert lib.pn_group_create_smallm(None, 1, ctypes.byref(h)) == PN_EINVAL
 
 
+def _in_thread(fn):
+    import threading
+    out = {}
+    t = threading.Thread(target=lambda: out.setdefault("v", fn()))
+    t.start()
+    t.join()
+    return out["v"]
+
+
 def test_smallm_math_setting():
+    """The arithmetic selection belongs to the calling host thread."""
     assert B.pn_get_smallm_math() == "mfma"
     assert B.pn_set_smallm_math(7, check=False) == PN_EINVAL
     assert B.pn_get_smallm_math() == "mfma"
     B.pn_set_smallm_math("valu")
-    assert B.pn_get_smallm_math() == "valu"
-    B.pn_set_smallm_math("mfma")
+    try:
+        assert B.pn_get_smallm_math() == "valu"
+        # another thread starts from the default and its choice stays its own
+        assert _in_thread(B.pn_get_smallm_math) == "mfma"
+        assert _in_thread(lambda: (B.pn_set_smallm_math("mfma"), B.pn_get_smallm_math())[1]) == "mfma"
+        assert B.pn_get_smallm_math() == "valu"
+    finally:
+        B.pn_set_smallm_math("mfma")
     assert B.pn_get_smallm_math() == "mfma"
 
 
 def test_gemv_kernel_setting():
+    """The M = 1 kernel selection belongs to the calling host thread."""
     assert B.pn_get_gemv_kernel() == "auto"
     assert B.pn_set_gemv_kernel(5, check=False) == PN_EINVAL
     assert B.pn_get_gemv_kernel() == "auto"
     B.pn_set_gemv_kernel("stream")
-    assert B.pn_get_gemv_kernel() == "stream"
-    B.pn_set_gemv_kernel("rows")
-    assert B.pn_get_gemv_kernel() == "rows"
-    B.pn_set_gemv_kernel("auto")
+    try:
+        assert B.pn_get_gemv_kernel() == "stream"
+        assert _in_thread(B.pn_get_gemv_kernel) == "auto"
+        assert _in_thread(lambda: (B.pn_set_gemv_kernel("rows"), B.pn_get_gemv_kernel())[1]) == "rows"
+        assert B.pn_get_gemv_kernel() == "stream"
+        B.pn_set_gemv_kernel("rows")
+        assert B.pn_get_gemv_kernel() == "rows"
+    finally:
+        B.pn_set_gemv_kernel("auto")
     assert B.pn_get_gemv_kernel() == "auto"

@@ -22,7 +22,7 @@ from oracle import pnref  # noqa: E402
 def test_prefill_split_k_graph_replays():
     t, n, k, m = "pn4t", 1024, 5120, 96  # four output tiles: the launch splits K
     g = np.random.default_rng(31)
-    w = synth.random_blocks(g, t, n, k)
+    w = synth.random_blocks(g, t, n, k, unused_bits=True)
     xm = synth.activation(g, k, m)
     y64, a = pnref.gemm_f64(t, w, n, k, xm)
     wd = dev(w.reshape(-1))
@@ -50,7 +50,7 @@ def test_rotated_plan_graph_replays():
     host, probs = [], []
     for i, (t, n, k) in enumerate(specs):
         g = np.random.default_rng([41, i])
-        w = synth.random_blocks(g, t, n, k)
+        w = synth.random_blocks(g, t, n, k, unused_bits=True)
         host.append((t, w, n, k, g))
         probs.append((t, dev(w.reshape(-1)), n, k, dev(synth.activation(g, k)),
                       torch.empty(n, dtype=torch.float32, device="cuda")))
@@ -104,7 +104,7 @@ def test_row_tile_plan_graph_replays():
     host, probs = [], []
     for i, (t, n, k) in enumerate(specs):
         g = np.random.default_rng([43, i])
-        w = synth.random_blocks(g, t, n, k)
+        w = synth.random_blocks(g, t, n, k, unused_bits=True)
         host.append((t, w, n, k, g))
         probs.append((t, dev(w.reshape(-1)), n, k, dev(synth.activation(g, k)),
                       torch.empty(n, dtype=torch.float32, device="cuda")))
@@ -135,7 +135,7 @@ def test_dma_smallm_plan_graph_replays():
     host, probs = [], []
     for i, (t, n, k, m) in enumerate(specs):
         g = np.random.default_rng([47, i])
-        w = synth.random_blocks(g, t, n, k)
+        w = synth.random_blocks(g, t, n, k, unused_bits=True)
         host.append((t, w, n, k, m, g))
         probs.append((t, dev(w.reshape(-1)), n, k, dev(synth.activation(g, k, m)), k, m,
                       torch.empty((m, n), dtype=torch.float32, device="cuda"), n))

@@ -43,7 +43,7 @@ SHAPES = [("pn3t", 256, 5120, 1), ("pn3t", 256, 5120, 17), ("pn3t", 256, 5120, 3
 @pytest.mark.parametrize("t,n,k,m", SHAPES)
 def test_prefill_matches_oracle(t, n, k, m):
     g = np.random.default_rng([n, k, m])
-    w = synth.random_blocks(g, t, n, k)
+    w = synth.random_blocks(g, t, n, k, unused_bits=True)
     xm = synth.activation(g, k, m)
     say("prefill %s N=%d K=%d M=%d" % (t, n, k, m))
     y = gpu_prefill(t, w, n, k, xm)
@@ -54,7 +54,7 @@ def test_prefill_matches_oracle(t, n, k, m):
 def test_prefill_leading_dimensions():
     g = np.random.default_rng(5)
     t, n, k, m = "pn4t", 200, 1024, 150
-    w = synth.random_blocks(g, t, n, k)
+    w = synth.random_blocks(g, t, n, k, unused_bits=True)
     xm = synth.activation(g, k, m)
     say("prefill ldx/ldy")
     y = gpu_prefill(t, w, n, k, xm, ldx=1048, ldy=203)
@@ -76,21 +76,49 @@ def test_prefill_zero_codes_and_outliers(t):
     xm[3, 5::89] = np.float16(-65504.0)
     say("prefill zero codes %s" % t)
     assert np.all(gpu_prefill(t, w, 40, k, xm) == 0)
-    w2 = synth.random_blocks(g, t, 140, k)
+    w2 = synth.random_blocks(g, t, 140, k, unused_bits=True)
     say("prefill outliers %s" % t)
     y64, a = pnref.gemm_f64(t, w2, 140, k, xm)
     assert_gemv_close(gpu_prefill(t, w2, 140, k, xm), y64, a, "prefill outliers")
 
 
-def test_prefill_full_size_sampled():
-    """The gate projection's shape (pn3t 17408 x 5120) with a 512-token
-    prompt: every output of sampled weight rows (first, last, random)."""
-    t, n, k, m = "pn3t", 17408, 5120, 512
-    g = np.random.default_rng(21)
-    w = synth.random_blocks(g, t, n, k)
+@pytest.mark.parametrize("t", ["pn3t", "pn4t"])
+def test_prefill_subnormal_activations(t):
+    """fp16-subnormal activations: row 0 of X is 2^-24 e_k (exact: the decoded
+    column times 2^-24), row 1 all subnormal, row 2 mixed, the rest N(0, 1).
+    A kernel that flushed subnormal inputs to zero would return zeros."""
+    g = np.random.default_rng(44)
+    n, k, m = 300, WPB[t] * 64, 130
+    w = synth.random_blocks(g, t, n, k, unused_bits=True)
     xm = synth.activation(g, k, m)
-    say("prefill full size %s %dx%d M=%d" % (t, n, k, m))
+    kk = 17 * WPB[t] + 5
+    xm[0] = 0
+    xm[0, kk] = np.uint16(1).view(np.float16)
+    for r, mix in ((1, False), (2, True)):
+        bits = g.integers(1, 1024, size=k).astype(np.uint16) | (g.integers(0, 2, size=k).astype(np.uint16) << 15)
+        xm[r] = bits.view(np.float16)
+        if mix:
+            xm[r, ::3] = synth.activation(g, k)[::3]
+    say("prefill subnormal activations %s" % t)
     y = gpu_prefill(t, w, n, k, xm)
-    rows = np.array(sorted(set([0, 1, 127, 128, n - 1] + list(g.integers(0, n, 11)))))
-    y64, a = pnref.gemm_f64(t, w[rows], len(rows), k, xm)
-    assert_gemv_close(y[:, rows], y64, a, "prefill full size")
+    dense = pnref.dequantize(t, w, n, k).astype(np.float64)
+    want = (dense[:, kk] * 2.0 ** -24).astype(np.float32)
+    assert np.array_equal((y[0] + 0.0).view(np.uint32), (want + 0.0).view(np.uint32)), "one-hot 2^-24"
+    y64, a = pnref.gemm_f64(t, w, n, k, xm)
+    assert np.all(a[1:3] > 0)
+    assert_gemv_close(y, y64, a, "prefill subnormal activations")
+
+
+def test_prefill_layer_full_size():
+    """Every product of one 27B-shaped layer (q, k, v, o, gate, up, down) with
+    a 512-token prompt chunk, as the benchmark runs it (k, v and o split K
+    over the CUs): every output against the oracle."""
+    m = 512
+    g = np.random.default_rng(21)
+    for name, t, n, k in synth.SWEEP_LAYER:
+        w = synth.random_blocks(g, t, n, k, unused_bits=True)
+        xm = synth.activation(g, k, m)
+        say("prefill full size %s %s %dx%d M=%d" % (name, t, n, k, m))
+        y = gpu_prefill(t, w, n, k, xm)
+        y64, a = pnref.gemm_f64(t, w, n, k, xm)
+        assert_gemv_close(y, y64, a, "prefill full size %s" % name)

@@ -112,7 +112,7 @@ def test_rotated_group(kernel):
     host, probs, flags = [], [], []
     for i, (t, n, k, rot) in enumerate(specs):
         g = np.random.default_rng([17, i])
-        w = synth.random_blocks(g, t, n, k)
+        w = synth.random_blocks(g, t, n, k, unused_bits=True)
         x = synth.activation(g, k)
         y = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
         xd = dev(x)

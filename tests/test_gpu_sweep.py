@@ -1,7 +1,9 @@
 """Full-size parity on the 64-layer 27B-shaped sweep (10.16 GB of packed
 weights), in the launch configurations the benchmark times.  The oracle
-computes sampled rows of every one of the 448 matrices (first, last and
-seeded random rows), kept aside while the weights are generated."""
+computes every output row of all 448 matrices (its fp64 sums and sum|w x|,
+taken while the weights are generated), and every row of the GPU's output is
+checked against them.  pn3t words carry random junk in their unused bits 15
+and 31, which every reader must ignore."""
 import numpy as np
 import pytest
 
@@ -15,23 +17,37 @@ from bit_quantized_decode_pn3t_amd import _binding as B  # noqa: E402
 from bit_quantized_decode_pn3t_amd import sweep as S  # noqa: E402
 from oracle import pnref  # noqa: E402
 
-ROWS = 6
+# the kernel each M = 1 schedule runs at these shapes
+M1_VARIANT = {"token": "gemv_rows_group", "token_rot": "gemv_rows_group", "layer": "gemv_stream_group",
+              "gemv": "gemv_stream"}
 
 
-def _check_samples(sw, store, m=None, rotated=False):
-    outs = {(e["layer"], e["mat"]): e["y"].cpu().numpy() for e in sw.mats}
-    worst = 0.0
-    for key, smp in store.items():
-        y = outs[key]
-        n_rows = len(smp["rows"])
-        if m is None:
-            x = pnref.rotate(smp["x"]) if rotated else smp["x"]
-            y64, a = pnref.gemv_f64(smp["type"], smp["W"], n_rows, smp["K"], x)
-            worst = max(worst, assert_gemv_close(y[smp["rows"]], y64, a, "sweep %s" % (key,)))
+def oracle_rows(store, rotated=False):
+    """Callback for Sweep(sample=...): the oracle's y64 and sum|w x| for every
+    row of the matrix (and, with `rotated`, for its rotated input too)."""
+    def sample(rec):
+        key = (rec["layer"], rec["mat"])
+        t, n, k, w, x = rec["type"], rec["N"], rec["K"], rec["W"], rec["x"]
+        if x.ndim == 1:
+            ent = {"plain": pnref.gemv_f64(t, w, n, k, x)}
+            if rotated:
+                ent["rot"] = pnref.gemv_f64(t, w, n, k, pnref.rotate(x))
         else:
-            y64, a = pnref.gemm_f64(smp["type"], smp["W"], n_rows, smp["K"], smp["x"])
-            worst = max(worst, assert_gemv_close(y[:, smp["rows"]], y64, a, "sweep M=8 %s" % (key,)))
-    return worst
+            ent = {"plain": pnref.gemm_f64(t, w, n, k, x)}
+        store[key] = ent
+    return sample
+
+
+def check_all_rows(sw, store, which="plain"):
+    """Every output of every matrix within 1e-5 * sum|w x| of the oracle."""
+    worst, rows = 0.0, 0
+    for e in sw.mats:
+        key = (e["layer"], e["mat"])
+        y64, a = store[key][which]
+        y = e["y"].cpu().numpy()
+        worst = max(worst, assert_gemv_close(y, y64, a, "sweep %s %s" % (which, key)))
+        rows += y.size
+    return worst, rows
 
 
 @pytest.fixture(scope="module")
@@ -39,8 +55,8 @@ def sweep_m1():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     store = {}
-    say("sweep M=1: generating 64 layers")
-    sw = S.Sweep(sample=lambda rec: S.sample_rows(rec, ROWS, store))
+    say("sweep M=1: generating 64 layers and the oracle's rows")
+    sw = S.Sweep(sample=oracle_rows(store, rotated=True), unused_bits=True)
     say("sweep M=1: %.2f GB of weights resident" % (sw.weight_bytes / 1e9))
     yield sw, store
     sw.close()
@@ -48,7 +64,7 @@ def sweep_m1():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("schedule", ["layer", "token", "gemv", "token_rot"])
+@pytest.mark.parametrize("schedule", ["token", "layer", "gemv", "token_rot"])
 def test_sweep_m1(sweep_m1, schedule):
     sw, store = sweep_m1
     for e in sw.mats:
@@ -56,21 +72,28 @@ def test_sweep_m1(sweep_m1, schedule):
     say("sweep M=1 schedule %s" % schedule)
     sw.step(schedule)
     sync()
-    worst = _check_samples(sw, store, rotated=schedule == "token_rot")
-    say("sweep M=1 %s: worst |y-y64|/sum|wx| = %.3g" % (schedule, worst))
+    assert B.pn_variant_name(B.pn_last_variant()) == M1_VARIANT[schedule]
+    worst, rows = check_all_rows(sw, store, "rot" if schedule == "token_rot" else "plain")
+    assert rows == 64 * (6144 + 2 * 1024 + 5120 + 2 * 17408 + 5120)
+    say("sweep M=1 %s: %d rows, worst |y-y64|/sum|wx| = %.3g" % (schedule, rows, worst))
 
 
-def test_sweep_m1_graph(sweep_m1):
+@pytest.mark.parametrize("schedule", ["layer", "token"])
+def test_sweep_m1_graph(sweep_m1, schedule):
+    """A captured token (one launch) or layer (256 launches) schedule, replayed
+    three times with eager work between the replays: every row every time
+    (the token plan's tile counters must be reset by each run for the next)."""
     sw, store = sweep_m1
-    say("sweep M=1 graph replays")
-    g = sw.capture("layer")
+    say("sweep M=1 graph replays, %s schedule" % schedule)
+    g = sw.capture(schedule)
     for rep in range(3):
         for e in sw.mats:
             e["y"].fill_(float("nan"))
         sync()
         g.replay()
         sync()
-        _check_samples(sw, store)
+        check_all_rows(sw, store)
+    sw.graph = None
 
 
 @pytest.fixture(scope="module")
@@ -78,8 +101,8 @@ def sweep_m8():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     store = {}
-    say("sweep M=8: generating 64 layers")
-    sw = S.Sweep(m=8, sample=lambda rec: S.sample_rows(rec, ROWS, store))
+    say("sweep M=8: generating 64 layers and the oracle's rows")
+    sw = S.Sweep(m=8, sample=oracle_rows(store), unused_bits=True)
     yield sw, store
     sw.close()
     del sw
@@ -91,7 +114,7 @@ def test_sweep_m8(sweep_m8, math):
     """M = 8 over the full sweep: one grouped launch per token (the benchmark's
     configuration) and one launch per matrix, with the given arithmetic (and
     for MFMA, the library's kernel choice, gemm_rows for these shapes, or
-    gemm_stream forced)."""
+    gemm_stream forced).  Every one of the 27.3 M outputs is checked."""
     sw, store = sweep_m8
     B.pn_set_smallm_math("valu" if math == "valu" else "mfma")
     B.pn_set_gemv_kernel("stream" if math == "mfma_stream" else "auto")
@@ -105,8 +128,8 @@ def test_sweep_m8(sweep_m8, math):
             sw.step(schedule)
             sync()
             assert B.pn_variant_name(B.pn_last_variant()) == kernel + ("_group" if schedule == "token" else "")
-            worst = _check_samples(sw, store, m=8)
-            say("sweep M=8 %s %s: worst %.3g" % (math, schedule, worst))
+            worst, rows = check_all_rows(sw, store)
+            say("sweep M=8 %s %s: %d outputs, worst %.3g" % (math, schedule, rows, worst))
     finally:
         B.pn_set_smallm_math("mfma")
         B.pn_set_gemv_kernel("auto")
