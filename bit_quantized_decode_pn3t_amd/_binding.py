@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpn.so")
 EXPORTS = ("pn_weights_per_block", "pn_row_bytes", "pn_gemv", "pn_gemv2",
            "pn_gemm_smallm", "pn_set_smallm_math", "pn_get_smallm_math", "pn_set_gemv_kernel",
            "pn_get_gemv_kernel", "pn_dequantize", "pn_rotate", "pn_gemm_prefill",
-           "pn_group_create", "pn_group_create_smallm", "pn_group_run", "pn_group_destroy",
+           "pn_group_create", "pn_group_create_smallm", "pn_group_run", "pn_group_destroy", "pn_gemv_batch",
            "pn_read_probe_scratch_bytes", "pn_read_probe", "pn_status_str", "pn_last_variant",
            "pn_variant_name")
 
@@ -100,6 +100,8 @@ def lib():
     L.pn_group_run.restype = i32
     L.pn_group_destroy.argtypes = [vp]
     L.pn_group_destroy.restype = None
+    L.pn_gemv_batch.argtypes = [ctypes.POINTER(pn_gemv_desc), i32, vp]
+    L.pn_gemv_batch.restype = i32
     L.pn_read_probe_scratch_bytes.argtypes = []
     L.pn_read_probe_scratch_bytes.restype = ctypes.c_size_t
     L.pn_read_probe.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t), vp]
@@ -268,6 +270,22 @@ def pn_group_create(problems):
 
 def pn_group_create_smallm(problems):
     return Group(problems, smallm=True)
+
+
+BATCH_MAX_PROBLEMS = 32  # PN_BATCH_MAX_PROBLEMS
+BATCH_MAX_ROWS = 65536 * 16  # PN_BATCH_MAX_ROWS
+
+
+def pn_gemv_batch(problems, stream=None, check=True):
+    """Run (pn_type, W, N, K, x, y) problems as one launch with no plan and no
+    allocation (the library's static per-device batch buffer holds the plan)."""
+    arr = (pn_gemv_desc * max(len(problems), 1))()
+    for i, (t, W, N, K, x, y) in enumerate(problems):
+        arr[i] = pn_gemv_desc(_ptr(W), _ptr(x), _ptr(y), N, K, _t(t), 0)
+    st = lib().pn_gemv_batch(arr, len(problems), _stream(stream))
+    if check:
+        _check(st, "pn_gemv_batch")
+    return st
 
 
 def pn_read_probe_scratch_bytes():

@@ -733,6 +733,37 @@ bool set_rows_attr()
                hipSuccess;
 }
 
+// A batch plan written by a kernel (pn_gemv_batch): the problems travel in
+// the kernel arguments, sorted longest rows first, with the first tile of
+// each in the hand-out order; the kernel writes the problem table, the tile
+// order (as rows_group_create lays it out) and zeroed pool counters into
+// the batch buffer.
+struct RBatch {
+    RProb p[kBatchMaxProblems];
+    int32_t first[kBatchMaxProblems + 1];
+    int32_t count;
+    int32_t total;
+};
+static_assert((kPools + 1) * kCounterStride * sizeof(uint32_t) <= kBatchCounterBytes, "batch counters");
+static_assert(kBatchMaxProblems * sizeof(RProb) <= kBatchTableBytes, "batch table");
+static_assert(sizeof(RBatch) <= 2048, "batch kernel arguments");
+
+__global__ __launch_bounds__(256) void rows_batch_setup(RBatch b, uint8_t *buf)
+{
+    const int tid = blockIdx.x * 256 + threadIdx.x;
+    const int stride = gridDim.x * 256;
+    RProb *table = (RProb *)(buf + kBatchTableOff);
+    if (tid < b.count) table[tid] = b.p[tid];
+    uint32_t *lut = (uint32_t *)(buf + kBatchLutOff);
+    for (int t = tid; t < b.total; t += stride) {
+        int i = 0;
+        while (i + 1 < b.count && b.first[i + 1] <= t) ++i;
+        lut[t] = ((uint32_t)i << 20) | (uint32_t)(t - b.first[i]);
+    }
+    uint32_t *counters = (uint32_t *)buf;
+    for (int j = tid; j < (int)(kBatchCounterBytes / 4); j += stride) counters[j] = 0u;
+}
+
 pn_status rlaunch(const RArgs &a, hipStream_t s, int variant)
 {
     if (!once_per_device(kAttrRows, set_rows_attr)) return PN_ELAUNCH;
@@ -867,4 +898,45 @@ pn_status pn::host::rows_group_run(const pn_group *g, hipStream_t s)
     a.count = g->count;
     a.total_tiles = g->total_tiles;
     return rlaunch(a, s, kVarGroupRows);
+}
+
+pn_status pn::host::rows_batch_launch(const pn_gemv_desc *descs, int count, uint8_t *buf, hipStream_t s)
+{
+    if (count < 1 || count > kBatchMaxProblems) return PN_EUNSUPPORTED;
+    RBatch b;
+    memset(&b, 0, sizeof(b));
+    int order[kBatchMaxProblems];
+    int maxwin = 0;
+    RProb p[kBatchMaxProblems];
+    for (int i = 0; i < count; ++i) {
+        const pn_gemv_desc &e = descs[i];
+        rfill(p[i], e.type, e.W, e.N, e.K, e.x, e.y);
+        if (p[i].nwin > maxwin) maxwin = p[i].nwin;
+    }
+    // longest rows first, as rows_group_create orders the tiles
+    int n = 0;
+    for (int w = maxwin; w >= 1; --w)
+        for (int i = 0; i < count; ++i)
+            if (p[i].nwin == w) order[n++] = i;
+    int64_t total = 0;
+    for (int j = 0; j < count; ++j) {
+        b.p[j] = p[order[j]];
+        b.first[j] = (int32_t)total;
+        total += b.p[j].tiles;
+    }
+    if (total > kBatchMaxTiles) return PN_EUNSUPPORTED;
+    b.first[count] = (int32_t)total;
+    b.count = count;
+    b.total = (int32_t)total;
+    const int grid = (int)((total + 255) / 256) < 64 ? (int)((total + 255) / 256) : 64;
+    hipLaunchKernelGGL(rows_batch_setup, dim3((unsigned)(grid > 0 ? grid : 1)), dim3(256), 0, s, b, buf);
+    if (hipGetLastError() != hipSuccess) return PN_ELAUNCH;
+    RArgs a;
+    memset(&a, 0, sizeof(a));
+    a.table = (const PN_CONST RProb *)(buf + kBatchTableOff);
+    a.lut = (const PN_CONST uint32_t *)(buf + kBatchLutOff);
+    a.counters = (uint32_t *)buf;
+    a.count = count;
+    a.total_tiles = (int32_t)total;
+    return rlaunch(a, s, kVarBatchRows);
 }

@@ -28,6 +28,8 @@ enum Variant {
     kVarPrefill = 12,
     kVarSmallMRows = 13,
     kVarGroupSmallMRows = 14,
+    kVarBatchRows = 15,
+    kVarBatchStream = 16,
 };
 
 extern thread_local int g_last_variant;
@@ -69,6 +71,18 @@ int smallm_math_choice();
 
 enum GroupKind { kGroupGemv = 0, kGroupSmallM = 1, kGroupGemvRows = 2 };
 
+// pn_gemv_batch: the plan of a batch lives in one per-device buffer of
+// kBatchBytes (a static device array): pool counters first (4 KiB apart),
+// then the problem table, then the tile hand-out order of the row-tile kernel.
+constexpr int kBatchMaxProblems = PN_BATCH_MAX_PROBLEMS;
+constexpr int kBatchMaxTiles = PN_BATCH_MAX_ROWS / 16;  // 16-row tiles
+constexpr size_t kBatchCounterBytes = 17 * 4096;
+constexpr size_t kBatchTableOff = kBatchCounterBytes;
+constexpr size_t kBatchTableBytes = 4096;
+constexpr size_t kBatchLutOff = kBatchTableOff + kBatchTableBytes;
+constexpr size_t kBatchBytes = kBatchLutOff + 4 * (size_t)kBatchMaxTiles;
+static_assert(kBatchBytes == PN_BATCH_BYTES, "PN_BATCH_BYTES in pn.h");
+
 }  // namespace host
 }  // namespace pn
 
@@ -99,6 +113,10 @@ pn_status rows_launch(int t, const void *W0, const void *W1, int64_t N, int64_t 
                       float *y1, hipStream_t s);
 pn_status rows_group_create(const pn_gemv_desc *descs, int count, pn_group **out);
 pn_status rows_group_run(const pn_group *g, hipStream_t s);
+// A batch (validated; every problem rows_ok, at most kBatchMaxTiles tiles) on
+// the row-tile kernel, its plan written into `buf` (kBatchBytes, device) by a
+// setup kernel ahead of the group launch, both on `s`.
+pn_status rows_batch_launch(const pn_gemv_desc *descs, int count, uint8_t *buf, hipStream_t s);
 // One block of a plan's activation rotation (pn_rotate.hip): src rotated
 // into dst, PN_ROTATE_BLOCK fp16 elements each.
 struct RotJob {

@@ -396,6 +396,25 @@ __global__ __launch_bounds__(256) void dequant(const uint8_t *W, int64_t N, int6
     }
 }
 
+// The plan of pn_gemv_batch (callers that cannot allocate): one buffer per
+// device, held until the process ends.  Host code never uses this name as an
+// address: batch_buffer() gets each device's copy with hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[kBatchBytes];
+
+// The register-pipeline kernel's batch plan: the problem table, copied from
+// the kernel arguments into the batch buffer.
+struct SBatch {
+    Prob p[kBatchMaxProblems];
+    int32_t count;
+};
+static_assert(kBatchMaxProblems * sizeof(Prob) <= kBatchTableBytes, "batch table");
+
+__global__ __launch_bounds__(64) void stream_batch_setup(SBatch b, uint8_t *buf)
+{
+    Prob *table = (Prob *)(buf + kBatchTableOff);
+    if ((int)threadIdx.x < b.count) table[threadIdx.x] = b.p[threadIdx.x];
+}
+
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
@@ -457,6 +476,28 @@ bool pn::host::once_per_device(AttrFlag f, bool (*set)())
     std::call_once(a.once, [&a, set]() { a.ok = set(); });
     return a.ok;
 }
+
+namespace {
+struct BatchBuf {
+    std::once_flag once;
+    uint8_t *ptr = nullptr;
+};
+BatchBuf g_batch[kMaxDevices];
+
+// The current device's copy of `scratch` (looked up once per device, with
+// that device current), or null if the lookup failed.
+uint8_t *batch_buffer()
+{
+    const int dev = current_device();
+    if (dev < 0) return nullptr;
+    BatchBuf &b = g_batch[dev];
+    std::call_once(b.once, [&b]() {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess) b.ptr = (uint8_t *)p;
+    });
+    return b.ptr;
+}
+}  // namespace
 
 int pn::host::gemv_kernel_choice() { return t_gemv_kernel; }
 int pn::host::smallm_math_choice() { return t_smallm_math; }
@@ -826,6 +867,56 @@ void pn_group_destroy(pn_group *g)
     free(g);
 }
 
+pn_status pn_gemv_batch(const pn_gemv_desc *descs, int count, void *stream)
+{
+    if (!descs || count < 1) return PN_EINVAL;
+    if (count > kBatchMaxProblems) return PN_EUNSUPPORTED;
+    bool all_rows = true;
+    int64_t rows_total = 0;
+    for (int i = 0; i < count; ++i) {
+        const pn_gemv_desc &e = descs[i];
+        if (e.flags & ~PN_DESC_ROTATE) return PN_EINVAL;
+        if (e.flags & PN_DESC_ROTATE) return PN_EUNSUPPORTED;  // a rotated copy would need a buffer
+        const pn_status st = check_matrix(e.type, e.W, e.N, e.K);
+        if (st != PN_OK) return st;
+        if (!e.x || !e.y) return PN_EINVAL;
+        if (!aligned4(e.x) || !aligned4(e.y)) return PN_EALIGN;
+        all_rows = all_rows && rows_ok(e.type, e.W, e.K, e.x);
+        rows_total += rows_tiles(e.N);
+    }
+    const bool rows = all_rows && rows_pays(rows_total);
+    if (rows && rows_total > kBatchMaxTiles) return PN_EUNSUPPORTED;
+    SBatch b;
+    int lds = 0;
+    bool v2 = true;
+    int64_t tiles = 0;
+    if (!rows) {
+        memset(&b, 0, sizeof(b));
+        for (int i = 0; i < count; ++i) {
+            const pn_gemv_desc &e = descs[i];
+            b.p[i] = make_prob(e.type, e.W, e.N, e.K, e.x, e.y);
+            if (!stream_ok(b.p[i])) return PN_EUNSUPPORTED;
+            v2 = v2 && stream_v2(b.p[i]);
+            if (lds_bytes_for(b.p[i]) > lds) lds = lds_bytes_for(b.p[i]);
+        }
+        tiles = plan_tiles(b.p, count, lds);
+        if (tiles < 0) return PN_EUNSUPPORTED;
+        b.count = count;
+    }
+    uint8_t *buf = batch_buffer();
+    if (!buf) return PN_ELAUNCH;
+    const hipStream_t s = (hipStream_t)stream;
+    if (rows) return rows_batch_launch(descs, count, buf, s);
+    hipLaunchKernelGGL(stream_batch_setup, dim3(1), dim3(64), 0, s, b, buf);
+    if (hipGetLastError() != hipSuccess) return PN_ELAUNCH;
+    StreamArgs a;
+    memset(&a, 0, sizeof(a));
+    a.table = (const Prob *)(buf + kBatchTableOff);
+    a.count = count;
+    a.total_tiles = (int32_t)tiles;
+    return launch_stream(a, lds, v2, s, kVarBatchStream);
+}
+
 const char *pn_status_str(pn_status e)
 {
     switch (e) {
@@ -878,6 +969,8 @@ const char *pn_variant_name(int v)
     case kVarPrefill: return "gemm_prefill";
     case kVarDequant: return "dequant";
     case kVarGroupStream: return "gemv_stream_group";
+    case kVarBatchRows: return "gemv_rows_batch";
+    case kVarBatchStream: return "gemv_stream_batch";
     }
     return "unknown";
 }

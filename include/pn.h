@@ -251,6 +251,30 @@ pn_status pn_group_run(const pn_group *g, void *stream);
 /* Free a plan (NULL is allowed).  Synchronises the device first. */
 void pn_group_destroy(pn_group *g);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops or harnesses that forbid hipMalloc): the problems of
+ * a pn_group_create plan, run at once without a plan.  Results are those of
+ * pn_group_create + pn_group_run on the same descriptors (the same kernel
+ * choice and tile order; no PN_DESC_ROTATE entries).
+ *
+ * The plan (problem table, tile order, tile-pool counters) is written into a
+ * library-owned device buffer of PN_BATCH_BYTES by one small kernel ahead of
+ * the GEMV launch, both on `stream`; the buffer is a static device array, one
+ * per GPU, held until the process ends.  The call allocates nothing and takes
+ * the descriptors (a host array) by value.  Every call on a GPU shares that
+ * GPU's buffer: calls on one stream are ordered, but calls that overlap on
+ * one GPU (two streams, or other host threads) race and must not be made.
+ *   count : 1..PN_BATCH_MAX_PROBLEMS, else PN_EINVAL (< 1) or
+ *           PN_EUNSUPPORTED (too many)
+ *   rows  : on the row-tile kernel at most PN_BATCH_MAX_ROWS rows in all
+ *           (16-row tiles), else PN_EUNSUPPORTED
+ * Other checks and errors as pn_group_create (PN_DESC_ROTATE entries return
+ * PN_EUNSUPPORTED). */
+#define PN_BATCH_MAX_PROBLEMS 32
+#define PN_BATCH_MAX_ROWS (65536 * 16)
+#define PN_BATCH_BYTES (17 * 4096 + 4096 + 4 * 65536)
+pn_status pn_gemv_batch(const pn_gemv_desc *descs, int count, void *stream);
+
 /* Streaming-read probe: the practical HBM read ceiling of the device,
  * measured in the same harness as the GEMV (the v100-skinny README, "Kernel
  * benchmarks", rates its kernels against a measured read-only ceiling).  One

@@ -48,14 +48,15 @@ def test_host_helpers():
 def test_variant_names():
     """Every kernel the library can report has its own name; unknown ids are
     reported as such rather than as a kernel."""
-    names = [B.pn_variant_name(v) for v in range(15)]
+    names = [B.pn_variant_name(v) for v in range(17)]
     assert names[0] == "none"
     assert len(set(names)) == len(names), names
     for expect in ("gemv_rows", "gemv_rows_group", "gemv_stream", "gemv_stream_group", "gemv_generic",
                    "gemm_stream_mfma", "gemm_stream_valu", "gemm_stream_mfma_group", "gemm_stream_valu_group",
-                   "gemm_rows_mfma", "gemm_rows_mfma_group", "gemm_prefill", "hadamard_rotate", "dequant"):
+                   "gemm_rows_mfma", "gemm_rows_mfma_group", "gemm_prefill", "hadamard_rotate", "dequant",
+                   "gemv_rows_batch", "gemv_stream_batch"):
         assert expect in names, expect
-    assert B.pn_variant_name(15) not in names[1:]
+    assert B.pn_variant_name(17) not in names[1:]
     assert B.pn_variant_name(-1) not in names[1:]
 
 
@@ -107,6 +108,26 @@ def test_group_host_checks():
     assert lib.pn_group_create(None, 1, ctypes.byref(h)) == PN_EINVAL
     assert lib.pn_group_run(None, None) == PN_EINVAL
     lib.pn_group_destroy(None)
+
+
+def test_batch_host_checks():
+    """pn_gemv_batch refuses, before anything reaches the GPU, a bad count,
+    more problems than its buffer holds, rotated inputs and the checks of
+    pn_group_create."""
+    lib = B.lib()
+    ok = ("pn3t", FAKE, 4, 640, FAKE, FAKE)
+    assert lib.pn_gemv_batch(None, 1, None) == PN_EINVAL
+    assert B.pn_gemv_batch([], stream=0, check=False) == PN_EINVAL
+    assert B.pn_gemv_batch([ok] * (B.BATCH_MAX_PROBLEMS + 1), stream=0, check=False) == -4
+    assert B.pn_gemv_batch([ok, ("pn3t", FAKE, 4, 81, FAKE, FAKE)], stream=0, check=False) == PN_ESHAPE
+    assert B.pn_gemv_batch([ok, ("pn4t", FAKE + 1, 4, 512, FAKE, FAKE)], stream=0, check=False) == PN_EALIGN
+    assert B.pn_gemv_batch([ok, ("pn3t", FAKE, 4, 640, None, FAKE)], stream=0, check=False) == PN_EINVAL
+    assert B.pn_gemv_batch([("pn3t", FAKE, 4, 240, FAKE, FAKE)], stream=0, check=False) == -4
+    arr = (B.pn_gemv_desc * 1)()
+    arr[0] = B.pn_gemv_desc(FAKE, FAKE, FAKE, 4, 5120, 0, B.DESC_ROTATE)
+    assert lib.pn_gemv_batch(arr, 1, None) == -4
+    arr[0] = B.pn_gemv_desc(FAKE, FAKE, FAKE, 4, 5120, 0, 2)
+    assert lib.pn_gemv_batch(arr, 1, None) == PN_EINVAL
 
 
 def test_prefill_host_checks():
