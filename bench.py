@@ -186,6 +186,54 @@ def prefill_timing(B, synth, torch, m=512):
             "per_matrix": per}
 
 
+def layer_read_floor(B, torch, layers):
+    """What the four-launches-per-layer schedule can reach at best: the
+    library's streaming-read probe in place of each of its launches ({q,k,v},
+    {o}, {gate,up}, {down} of every layer, one HIP graph, 8 rotating copies
+    of a layer's buffers so that every launch reads from HBM), no arithmetic.
+    The probe reads whole 1 KiB instructions per wave, so each launch reads
+    a little less than the group it stands for; the rate uses the bytes read."""
+    from bit_quantized_decode_pn3t_amd import sweep as S
+    from bit_quantized_decode_pn3t_amd import synth
+    sizes = [sum(synth.row_bytes(synth.SWEEP_LAYER[j][1], synth.SWEEP_LAYER[j][3]) * synth.SWEEP_LAYER[j][2]
+                 for j in grp) for grp in S.LAYER_GROUPS]
+    copies = 8
+    bufs = [[torch.ones(sz // 4096 * 4096, dtype=torch.uint8, device="cuda") for sz in sizes] for _ in range(copies)]
+    scratch = torch.empty(B.pn_read_probe_scratch_bytes() // 4, dtype=torch.int32, device="cuda")
+    got = []
+
+    def step():
+        got.clear()
+        for l in range(layers):
+            for b in bufs[l % copies]:
+                got.append(B.pn_read_probe(b, b.numel(), scratch, scratch.numel() * 4))
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = 10
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    nread = sum(got)
+    del g, bufs, scratch
+    torch.cuda.empty_cache()
+    return {"launches_per_token": len(got), "bytes_per_token": nread, "ms_per_token": round(ms, 4),
+            "gbps": round(nread / (ms * 1e-3) / 1e9, 1),
+            "note": "read probe in place of every launch of the layer schedule (HIP graph); "
+                    "the same bytes in one launch run at read_ceiling_gbps"}
+
+
 def host_read_gbps():
     """Host memory read rate (numpy sum over 1 GiB of uint64, best of 3)."""
     import numpy as np
@@ -449,6 +497,15 @@ def main():
     del buf, scratch
     torch.cuda.empty_cache()
     log("read ceiling %.1f GB/s" % read_ceiling)
+    layer_floor = None
+    if m is None and not args.no_secondary:
+        log("read floor of the four-launches-per-layer schedule")
+        layer_floor = layer_read_floor(B, torch, args.layers)
+        # time per launch beyond what its bytes take at the one-launch read rate
+        layer_floor["per_launch_overhead_us"] = round(
+            (layer_floor["ms_per_token"] * 1e-3 - layer_floor["bytes_per_token"] / (read_ceiling * 1e9))
+            / layer_floor["launches_per_token"] * 1e6, 2)
+        log("layer schedule read floor %.1f GB/s" % layer_floor["gbps"])
 
     per_config = None
     if not args.no_configs and m is None:
@@ -510,6 +567,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "other_schedules": secondary,
+        "layer_schedule_read_floor": layer_floor,
         "per_config": per_config,
         "prefill": prefill,
         "smallm_m8": smallm,

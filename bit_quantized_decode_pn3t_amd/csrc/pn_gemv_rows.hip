@@ -114,6 +114,12 @@ constexpr int kDma = kMainDma + kBndDma;        // DMA instructions per stage
 constexpr int kStage = 1024 * kDma;          // LDS bytes per stage
 constexpr int kXLoads = 5;                    // x loads per lane per stage
 constexpr int kLater = (kNS - 1) * (kDma + kXLoads);  // VMEM instructions issued after a stage
+// With one stage per wave every wait is for all loads in flight, so a stage
+// without work issues no loads at all (with two, every stage issues the same
+// instructions so that the counted waits stay exact).  Issuing a stage's 23
+// instructions is not free: a wave with nothing else in flight on its CU
+// takes about a microsecond to push them.
+constexpr bool kSkipIdle = kNS == 1;
 constexpr int kRing = kRWaves * kNS * kStage;  // 155,648 bytes of LDS (147,456 without the boundary region)
 constexpr int kMinTilesPerCu = 32;            // below this "auto" uses gemv_stream
 constexpr int kPools = 16;                    // tile pools of a group launch
@@ -432,15 +438,17 @@ __device__ __forceinline__ void dma_offsets(uint32_t (&vo)[kDma], int32_t S, int
 }
 
 // The cursor's window into a ring stage: kDma DMA instructions.  A cursor
-// without a tile issues them on an empty buffer range (they read nothing and
-// write zeros), and chunks past the end of a row in a partial last window
-// are given an out-of-range offset, so that nothing is read twice.  Every
-// stage is exactly kDma + kXLoads VMEM instructions (issue_x below).  The
+// without a tile issues none with one stage per wave (kSkipIdle), and with
+// two issues them on an empty buffer range (they read nothing and write
+// zeros), so that every stage is exactly kDma + kXLoads VMEM instructions
+// (issue_x below).  Chunks past the end of a row in a partial last window
+// are given an out-of-range offset, so that nothing is read twice.  The
 // instructions are issued in pieces (dma_part), set up once (dma_setup).
 struct Dma {
     __amdgpu_buffer_rsrc_t wr;
     uint32_t soff;  // the window's byte offset in the tile's rows
     uint32_t nck;   // valid chunks per row
+    bool on;        // the instructions are issued
 };
 
 __device__ __forceinline__ Dma dma_setup(const Cursor &c)
@@ -456,12 +464,14 @@ __device__ __forceinline__ Dma dma_setup(const Cursor &c)
     d.soff = (uint32_t)(c.win * kWindow);
     const int32_t pv = c.P - 4 * c.win;  // periods of this window in the row
     d.nck = pv >= 4 ? 68u : 17u * (uint32_t)pv;
+    d.on = live || !kSkipIdle;
     return d;
 }
 
 template <int I0, int I1>
 __device__ __forceinline__ void dma_part(const Dma &d, uint8_t *stage, const uint32_t (&vo)[kDma], int lane)
 {
+    if (!d.on) return;
 #pragma unroll
     for (int i = I0; i < (I1 < kMainDma ? I1 : kMainDma); ++i) {
         uint32_t row;
@@ -493,9 +503,12 @@ __device__ __forceinline__ void issue_x(const Cursor &c, uint32_t xlane, u32x4 (
     const uint32_t px = c.type == 0 ? 1280u : 1024u;  // x bytes per period
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(uniform_ptr(c.x), (uint32_t)uniform((int32_t)(live ? (uint32_t)c.P * px : 0u)));
     const uint32_t xsoff = 4u * (uint32_t)c.win * px;
+    if (live || !kSkipIdle) {
 #pragma unroll
-    for (int i = 0; i < kXLoads; ++i)
-        xs[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(xlane + 256u * i), (int)xsoff, 0));
+        for (int i = 0; i < kXLoads; ++i)
+            xs[i] = __builtin_bit_cast(u32x4,
+                                       __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(xlane + 256u * i), (int)xsoff, 0));
+    }
     sl.y = c.y + kTileRows * c.tile;
     sl.live = live ? 1 : 0;
     sl.done = c.state == kDone ? 1 : 0;

@@ -45,7 +45,8 @@ __global__ __launch_bounds__(kProbeThreads) void read_probe(const uint8_t *buf, 
     uint8_t *ring = lds + wave * 2 * kProbeStage;
     const __amdgpu_buffer_rsrc_t r =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(buf + gw * span), 0, (int)span, 0x00020000);
-    const int n = (int)(span / kProbeStage);  // stages of this wave (span is a multiple)
+    const int n = (int)((span + kProbeStage - 1) / kProbeStage);  // stages of this wave; the last may
+                                                                    // run past the span (read nothing)
     uint32_t acc = 0;
     probe_issue(r, ring, lane, 0);
     probe_issue(r, ring + kProbeStage, lane, 1);  // past the end: out of range, reads nothing
@@ -102,8 +103,8 @@ pn_status pn_read_probe(const void *buf, size_t bytes, void *scratch, size_t scr
     const uint64_t waves = grid * kProbeWaves;
     if (scratch_bytes < waves * 64 * sizeof(uint32_t)) return PN_ESHAPE;
     uint64_t span = bytes / waves;
-    span -= span % kProbeStage;
-    if (span < kProbeStage || span > 0x7fffffffu) return PN_ESHAPE;
+    span -= span % 1024;  // whole DMA instructions per wave
+    if (span < 1024 || span > 0x7fffffffu) return PN_ESHAPE;
     if (!pn::host::once_per_device(pn::host::kAttrProbe, set_probe_attr)) return PN_ELAUNCH;
     hipLaunchKernelGGL(read_probe, dim3((unsigned)grid), dim3(kProbeThreads), kProbeLds, (hipStream_t)stream,
                        (const uint8_t *)buf, (uint32_t)span, (uint32_t *)scratch);

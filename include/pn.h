@@ -279,7 +279,7 @@ pn_status pn_gemv_batch(const pn_gemv_desc *descs, int count, void *stream);
  * measured in the same harness as the GEMV (the v100-skinny README, "Kernel
  * benchmarks", rates its kernels against a measured read-only ceiling).  One
  * launch reads `*bytes_read` bytes (the largest multiple of the launch's
- * granule not above `bytes`, at least 16 KiB per wave) from `buf` with
+ * granule, 1 KiB per wave, not above `bytes`) from `buf` with
  * 16-byte nontemporal DMA loads into LDS (each wave a contiguous share) and
  * writes a checksum word per lane to `scratch`.
  *   buf     : device, 16-byte aligned, `bytes` readable

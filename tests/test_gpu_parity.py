@@ -602,11 +602,12 @@ def test_smallm_group_periods(smallm_math):
     grp.close()
 
 
-def test_read_probe():
+@pytest.mark.parametrize("n", [64 << 20, 16711680])
+def test_read_probe(n):
     """The streaming-read probe reads what it reports and folds it exactly:
-    the XOR of all per-lane checksums equals the XOR of every word read."""
-    say("read probe")
-    n = 64 << 20
+    the XOR of all per-lane checksums equals the XOR of every word read
+    (16,711,680 bytes: each wave's share ends inside a 16 KiB stage)."""
+    say("read probe %d bytes" % n)
     rs = np.random.default_rng(9)
     host = rs.integers(0, 2 ** 32, size=n // 4, dtype=np.uint32)
     buf = dev(host.view(np.uint8))
