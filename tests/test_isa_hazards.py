@@ -1,4 +1,4 @@
-"""Static checks of the row-tile kernel's hand-written instructions.
+"""Static checks of the kernels' instruction streams on gfx950.
 
 The row-tile GEMV issues v_dot2c_f32_f16 with a DPP broadcast operand from
 inline asm, so the compiler's hazard recognizer does not see them.  gfx950
@@ -9,7 +9,22 @@ accumulator and any other instruction that reads or writes that register
 A missing (b) drops the last product of a block: exactly the failure this
 test guards against.  Wait states are counted as the hardware does (an
 s_nop n is n + 1 of them).  The kernel is compiled to gfx950 assembly here (no GPU
-needed) and every such instruction is checked in straight-line code."""
+needed) and every such instruction is checked in straight-line code.
+
+MFMA accumulation chains: an MFMA that reads as its accumulator (SrcC) the
+result of an MFMA of another shape (v_mfma_f32_16x16x32_f16 after
+v_mfma_f32_16x16x16_f16, or the reverse) needs at least 5 wait states
+between them on MI355X, while a chain of one shape is forwarded with none.
+Measured: with the pair otherwise adjacent, 0 to 4 wait states gave wrong
+values in about half of the 256 outputs of a 16 x 16 tile, 5 or more gave
+the exact sums.  The compiler inserts none when the accumulator registers
+match exactly, as for a chain of one shape; a dropped pn3t variant of
+gemm_stream that ended a chain of two K = 32 steps with one K = 16 step got
+wrong sums that way.  The shipped MFMA kernels start every block's chain
+from a zero accumulator and keep one shape per chain; the check below walks
+the control-flow graph of each compiled kernel backwards from every
+accumulating MFMA and fails on a different-shape MFMA result reached within
+5 wait states."""
 import os
 import re
 import shutil
@@ -102,6 +117,175 @@ def find_hazards(asm):
                     break
                 ws += _wait_states(prev)
     return found
+
+
+MFMA_SHAPE_WAIT = 5  # wait states a different-shape MFMA result needs before it is read as SrcC
+BRANCHES = ("s_branch", "s_cbranch", "s_setpc", "s_endpgm")
+
+
+def _regs2(tok):
+    """Registers of an operand as (file, index) pairs: VGPRs and AGPRs."""
+    m = re.match(r"([va])\[(\d+):(\d+)\]$", tok)
+    if m:
+        return {(m.group(1), r) for r in range(int(m.group(2)), int(m.group(3)) + 1)}
+    m = re.match(r"([va])(\d+)$", tok)
+    return {(m.group(1), int(m.group(2)))} if m else set()
+
+
+def _blocks(asm):
+    """Basic blocks of every function in `asm`: lists of instructions, a
+    label (or None) per block and the successor block indices."""
+    blocks, labels = [[]], [None]
+    for raw in asm.splitlines():
+        line = raw.split(";")[0].strip()
+        if not line or line.startswith((".", "//")) and not line.endswith(":"):
+            continue
+        if line.endswith(":"):
+            blocks.append([])
+            labels.append(line[:-1])
+            continue
+        blocks[-1].append(line)
+        if line.startswith(BRANCHES):
+            blocks.append([])
+            labels.append(None)
+    index = {l: i for i, l in enumerate(labels) if l}
+    succ = []
+    for i, b in enumerate(blocks):
+        last = b[-1] if b else ""
+        op, args = _split(last) if last else ("", [])
+        out = []
+        if op.startswith(("s_branch", "s_cbranch")) and args and args[0] in index:
+            out.append(index[args[0]])
+        if not op.startswith(("s_branch", "s_setpc", "s_endpgm")) and i + 1 < len(blocks):
+            out.append(i + 1)
+        succ.append(out)
+    return blocks, labels, succ
+
+
+def find_mfma_shape_hazards(asm, need=MFMA_SHAPE_WAIT):
+    """Accumulating MFMAs that can read the result of an MFMA of another
+    opcode fewer than `need` wait states after it, on some path."""
+    blocks, labels, succ = _blocks(asm)
+    pred = [[] for _ in blocks]
+    for i, out in enumerate(succ):
+        for j in out:
+            pred[j].append(i)
+    found = []
+    for bi, b in enumerate(blocks):
+        for ii, line in enumerate(b):
+            op, args = _split(line)
+            if not op.startswith("v_mfma") or len(args) < 4:
+                continue
+            srcc = _regs2(args[3].split()[0])
+            if not srcc:
+                continue  # a constant accumulator: a chain starts here
+            # walk back over every path until `need` wait states have passed
+            todo = [(bi, ii - 1, 0)]
+            seen = set()
+            while todo:
+                cb, ci, ws = todo.pop()
+                if (cb, ci, ws) in seen:
+                    continue
+                seen.add((cb, ci, ws))
+                while ci >= 0 and ws < need:
+                    prev = blocks[cb][ci]
+                    pop, pa = _split(prev)
+                    dst = _regs2(pa[0].split()[0]) if pa else set()
+                    if dst & srcc:
+                        if pop.startswith("v_mfma") and pop != op:
+                            found.append("%s -> %s after %d wait states" % (prev, line, ws))
+                        break  # the accumulator's producer on this path
+                    ws += _wait_states(prev)
+                    ci -= 1
+                else:
+                    if ws < need:
+                        for p in pred[cb]:
+                            todo.append((p, len(blocks[p]) - 1, ws))
+    return found
+
+
+def test_mfma_shape_checker_flags_a_planted_hazard():
+    planted = """
+_kernel:
+    v_mfma_f32_16x16x32_f16 v[0:3], v[4:7], v[8:11], 0
+    v_mfma_f32_16x16x32_f16 v[0:3], v[12:15], v[16:19], v[0:3]
+    v_mfma_f32_16x16x16_f16 v[0:3], v[20:21], v[22:23], v[0:3]
+    s_nop 4
+    v_mfma_f32_16x16x32_f16 v[24:27], v[4:7], v[8:11], v[0:3]
+.LBB0_1:
+    v_mfma_f32_16x16x16_f16 a[0:3], v[20:21], v[22:23], a[0:3]
+    s_nop 7
+    s_nop 7
+    v_add_f32_e32 v30, v31, v32
+    v_mfma_f32_16x16x32_f16 a[0:3], v[4:7], v[8:11], a[0:3]
+    s_cbranch_scc1 .LBB0_1
+    v_mfma_f32_16x16x32_f16 v[40:43], v[4:7], v[8:11], 0
+    v_mov_b32_e32 v40, 0
+    v_mfma_f32_16x16x16_f16 v[40:43], v[20:21], v[22:23], v[40:43]
+    s_endpgm
+"""
+    got = find_mfma_shape_hazards(planted)
+    # K=32 -> K=16 adjacent; the loop's K=32 -> its head's K=16 across the
+    # back edge (one wait state: the branch); not the K=16 -> K=32 after 5
+    # wait states, not the same-shape link, not after the v_mov rewrote v40
+    assert len(got) == 2, got
+    assert "v[0:3], v[12:15]" in got[0] and "v[20:21]" in got[0] and "after 0 wait states" in got[0]
+    assert "a[0:3], v[4:7]" in got[1] and "a[0:3], v[20:21]" in got[1] and "after 1 wait states" in got[1]
+
+
+SNIPPET = r"""
+#include <hip/hip_runtime.h>
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+template <int NOPS>
+__global__ void chain(const h8 *a8, const h4 *a4, f4 *out)
+{
+    const int l = threadIdx.x;
+    const h8 x0 = a8[l], x1 = a8[l + 64];
+    const h4 x2 = a4[l];
+    __builtin_amdgcn_sched_barrier(0);
+    f4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(x0, x1, (f4){0, 0, 0, 0}, 0, 0, 0);
+    if (NOPS) asm volatile("s_nop 4" : "+v"(d));
+    d = __builtin_amdgcn_mfma_f32_16x16x16f16(x2, x2, d, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    out[l] = d;
+}
+template __global__ void chain<0>(const h8 *, const h4 *, f4 *);
+template __global__ void chain<1>(const h8 *, const h4 *, f4 *);
+"""
+
+
+def _compile(tmp_path, src_path, name):
+    out = tmp_path / (name + ".s")
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "--cuda-device-only", "-S",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I" + os.path.join(ROOT, "include"), "-o", str(out), str(src_path)]
+    subprocess.run(cmd, check=True, capture_output=True, cwd=os.path.dirname(SRC))
+    return out.read_text()
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None, reason="no hipcc")
+def test_compiler_leaves_mixed_chain_unguarded(tmp_path):
+    """The case the check exists for: compiled with nothing in between, the
+    K = 16 step follows the K = 32 step that writes its accumulator within a
+    wait state or so (the compiler adds none for the accumulator); with an
+    s_nop 4 between (the compiler adds one more after the asm) the pair is
+    6 wait states apart and passes."""
+    src = tmp_path / "chain.hip"
+    src.write_text(SNIPPET)
+    asm = _compile(tmp_path, src, "chain")
+    got = find_mfma_shape_hazards(asm)
+    assert len(got) == 1, got
+    assert int(re.search(r"after (\d+) wait states", got[0]).group(1)) < MFMA_SHAPE_WAIT, got
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None, reason="no hipcc")
+@pytest.mark.parametrize("src,min_mfma", [("pn_smallm.hip", 16), ("pn_prefill.hip", 4)])
+def test_mfma_kernels_keep_one_shape_per_chain(tmp_path, src, min_mfma):
+    asm = _compile(tmp_path, os.path.join(os.path.dirname(SRC), src), src)
+    assert len(re.findall(r"^\s*v_mfma", asm, re.M)) >= min_mfma
+    assert find_mfma_shape_hazards(asm) == []
 
 
 def test_checker_flags_a_planted_hazard():
