@@ -24,6 +24,17 @@
 // two stages while the other is computed, and each wave decodes its 32
 // weight rows straight into B operands.
 //
+// Work.  One workgroup per CU, persistent.  The launch's tiles would leave
+// the last round of workgroups part empty (272 gate tiles on 256 CUs take
+// two rounds of the same length), so the tiles of whole rounds are dealt
+// whole (tile t to workgroup t mod G, plain stores) and each of the R
+// remaining tiles is shared by `ways` workgroups, each taking a slice of its
+// block pairs and adding its sums into Y with fp32 atomics, those tiles'
+// rows having been zeroed by a kernel ahead of the launch.  The slices of a
+// shared tile are then added in a different order from run to run (within
+// the tolerance); tiles dealt whole are stored plainly and come out the
+// same every run.
+//
 // Operand layouts (checked on the GPU: lane l of the 32 x 32 x 16 MFMA):
 // A row l % 32, k = 8 (l / 32) + e; B column l % 32, same k; result
 // register v holds row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.  So a
@@ -58,6 +69,10 @@ constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfM = 128;    // X rows per workgroup
 constexpr int kPfN = 256;    // weight rows per workgroup
 constexpr int kPairDw = 17;  // dwords per block pair
+#ifndef PN_PF_MAX_WAYS
+#define PN_PF_MAX_WAYS 8
+#endif
+constexpr int kPfMaxWays = PN_PF_MAX_WAYS;  // workgroups that may share one tile's block pairs
 // 32-row X tiles per wave: 4 (each wave decodes its own 32 weight rows and
 // multiplies them by all 128 X rows) or 2 (2 x 2 tiles: two waves decode the
 // same weight rows).  4 is 3-10 % faster: half the unpack work, twice the X
@@ -93,7 +108,9 @@ struct PfArgs {
     float *Y;
     int64_t ldx, ldy;
     int32_t N, M, S, pairs;  // S: row bytes; pairs: block pairs per row
-    int32_t splits;          // K slices (grid z); > 1: Y is zeroed first and the slices add into it
+    int32_t tn, tiles;       // tiles along N, tiles (tile t: N tile t % tn, M tile t / tn)
+    int32_t t1;              // tiles [0, t1) dealt whole, a whole number of rounds
+    int32_t ways;            // workgroups sharing each of tiles [t1, tiles) (0: none shared)
 };
 
 __device__ __forceinline__ half8_t cat4(half2_t a, half2_t b, half2_t c, half2_t d)
@@ -175,109 +192,128 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill(PfArgs a)
     const int wave = (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave % kWM, wn = wave / kWM;
     const int h = lane >> 5, c = lane & 31;
-    const int n0 = blockIdx.x * kPfN, m0 = blockIdx.y * kPfM;
-    const int xrows = a.M - m0 < kPfM ? a.M - m0 : kPfM;
-    const int wrows = a.N - n0 < kPfN ? a.N - n0 : kPfN;
     const uint32_t xrow = (uint32_t)a.ldx * 2u, wrow = (uint32_t)a.S;
-    const __amdgpu_buffer_rsrc_t xr = rsrc(a.X + (int64_t)m0 * a.ldx, (uint32_t)xrows * xrow);
-    const __amdgpu_buffer_rsrc_t wr = rsrc(a.W + (int64_t)n0 * a.S, (uint32_t)wrows * wrow);
-
-    float16_t acc[kMT][kNT];
-#pragma unroll
-    for (int i = 0; i < kMT; ++i)
-#pragma unroll
-        for (int j = 0; j < kNT; ++j) acc[i][j] = (float16_t){};
-
-    // this workgroup's slice of the block pairs
-    const int p0 = (int)((int64_t)a.pairs * blockIdx.z / a.splits);
-    const int p1 = (int)((int64_t)a.pairs * (blockIdx.z + 1) / a.splits);
     uint32_t xo[C::XPER], wo[C::WPER];
     pf_offsets<TYPE>(xo, wo, xrow, wrow, wave, lane);
-    stage_pair<TYPE>(lds, xr, wr, xo, wo, p0, wave);
-    for (int p = p0; p < p1; ++p) {
-        // this wave's loads of pair p have landed; after the barrier, every
-        // wave's have, and every wave is done with pair p - 1's stage
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+
+    // Block pairs [p0, p1) of tile t, stored (add = false) or added into Y.
+    auto piece = [&](int t, int p0, int p1, bool add) {
+        const int n0 = (t % a.tn) * kPfN, m0 = (t / a.tn) * kPfM;
+        const int xrows = a.M - m0 < kPfM ? a.M - m0 : kPfM;
+        const int wrows = a.N - n0 < kPfN ? a.N - n0 : kPfN;
+        const __amdgpu_buffer_rsrc_t xr = rsrc(a.X + (int64_t)m0 * a.ldx, (uint32_t)xrows * xrow);
+        const __amdgpu_buffer_rsrc_t wr = rsrc(a.W + (int64_t)n0 * a.S, (uint32_t)wrows * wrow);
+
+        float16_t acc[kMT][kNT];
+#pragma unroll
+        for (int i = 0; i < kMT; ++i)
+#pragma unroll
+            for (int j = 0; j < kNT; ++j) acc[i][j] = (float16_t){};
+
+        // every wave is done with the stages of the workgroup's last piece
         __syncthreads();
-        uint8_t *st = lds + ((p - p0) & 1) * C::STAGE;
-        if (p + 1 < p1) stage_pair<TYPE>(lds + ((p - p0 + 1) & 1) * C::STAGE, xr, wr, xo, wo, p + 1, wave);
-        const uint16_t *xs = (const uint16_t *)st;
-        const uint32_t *ws = (const uint32_t *)(st + C::XBYTES);
+        stage_pair<TYPE>(lds, xr, wr, xo, wo, p0, wave);
+        for (int p = p0; p < p1; ++p) {
+            // this wave's loads of pair p have landed; after the barrier, every
+            // wave's have, and every wave is done with pair p - 1's stage
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+            __syncthreads();
+            uint8_t *st = lds + ((p - p0) & 1) * C::STAGE;
+            if (p + 1 < p1) stage_pair<TYPE>(lds + ((p - p0 + 1) & 1) * C::STAGE, xr, wr, xo, wo, p + 1, wave);
+            const uint16_t *xs = (const uint16_t *)st;
+            const uint32_t *ws = (const uint32_t *)(st + C::XBYTES);
 
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            // decode: the lane's four words of block b, for its row of each N tile
-            half2_t u[kNT][4][TYPE == 0 ? 5 : 4];
-            float d[kNT];
-#pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) {
-                const uint32_t *pw = ws + (wn * 32 * kNT + nt * 32 + c) * kPairDw;
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    Unpack<TYPE>::run(pair_word(pw, b, TYPE == 0 ? 4 * h + j : h + 2 * j), u[nt][j]);
-                d[nt] = pair_scale(pw, b);
-            }
-            float16_t P[kMT][kNT];  // the block's fresh accumulators
-#pragma unroll
-            for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < kNT; ++nt) P[mt][nt] = (float16_t){};
-#pragma unroll
-            for (int s = 0; s < C::STEPS; ++s) {
-                half8_t B[kNT];
+            for (int b = 0; b < 2; ++b) {
+                // decode: the lane's four words of block b, for its row of each N tile
+                half2_t u[kNT][4][TYPE == 0 ? 5 : 4];
+                float d[kNT];
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt) {
-                    if constexpr (TYPE == 0)  // the lane's code pairs 4s .. 4s+3 (pair i: word i / 5, pair i % 5)
-                        B[nt] = cat4(u[nt][(4 * s) / 5][(4 * s) % 5], u[nt][(4 * s + 1) / 5][(4 * s + 1) % 5],
-                                     u[nt][(4 * s + 2) / 5][(4 * s + 2) % 5], u[nt][(4 * s + 3) / 5][(4 * s + 3) % 5]);
-                    else
-                        B[nt] = cat4(u[nt][s][0], u[nt][s][1], u[nt][s][2], u[nt][s][3]);
+                    const uint32_t *pw = ws + (wn * 32 * kNT + nt * 32 + c) * kPairDw;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        Unpack<TYPE>::run(pair_word(pw, b, TYPE == 0 ? 4 * h + j : h + 2 * j), u[nt][j]);
+                    d[nt] = pair_scale(pw, b);
+                }
+                float16_t P[kMT][kNT];  // the block's fresh accumulators
+#pragma unroll
+                for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < kNT; ++nt) P[mt][nt] = (float16_t){};
+#pragma unroll
+                for (int s = 0; s < C::STEPS; ++s) {
+                    half8_t B[kNT];
+#pragma unroll
+                    for (int nt = 0; nt < kNT; ++nt) {
+                        if constexpr (TYPE == 0)  // the lane's code pairs 4s .. 4s+3 (pair i: word i / 5, pair i % 5)
+                            B[nt] = cat4(u[nt][(4 * s) / 5][(4 * s) % 5], u[nt][(4 * s + 1) / 5][(4 * s + 1) % 5],
+                                         u[nt][(4 * s + 2) / 5][(4 * s + 2) % 5], u[nt][(4 * s + 3) / 5][(4 * s + 3) % 5]);
+                        else
+                            B[nt] = cat4(u[nt][s][0], u[nt][s][1], u[nt][s][2], u[nt][s][3]);
+                    }
+#pragma unroll
+                    for (int mt = 0; mt < kMT; ++mt) {
+                        const uint16_t *px = xs + (wm * 32 * kMT + mt * 32 + c) * (8 * C::XSL);
+                        const int k = TYPE == 0 ? 80 * b + 40 * h + 8 * s : 64 * b + 16 * s + 8 * h;
+                        const half8_t A = __builtin_bit_cast(half8_t, *(const u32x4 *)(px + k));
+#pragma unroll
+                        for (int nt = 0; nt < kNT; ++nt)
+                            P[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B[nt], P[mt][nt], 0, 0, 0);
+                    }
                 }
 #pragma unroll
-                for (int mt = 0; mt < kMT; ++mt) {
-                    const uint16_t *px = xs + (wm * 32 * kMT + mt * 32 + c) * (8 * C::XSL);
-                    const int k = TYPE == 0 ? 80 * b + 40 * h + 8 * s : 64 * b + 16 * s + 8 * h;
-                    const half8_t A = __builtin_bit_cast(half8_t, *(const u32x4 *)(px + k));
+                for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
                     for (int nt = 0; nt < kNT; ++nt)
-                        P[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B[nt], P[mt][nt], 0, 0, 0);
-                }
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) acc[mt][nt][v] = __builtin_fmaf(d[nt], P[mt][nt][v], acc[mt][nt][v]);
             }
-#pragma unroll
-            for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) acc[mt][nt][v] = __builtin_fmaf(d[nt], P[mt][nt][v], acc[mt][nt][v]);
         }
-    }
 
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
+        for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-            const int n = n0 + wn * 32 * kNT + nt * 32 + c;
+            for (int nt = 0; nt < kNT; ++nt) {
+                const int n = n0 + wn * 32 * kNT + nt * 32 + c;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int m = m0 + wm * 32 * kMT + mt * 32 + 8 * (v / 4) + 4 * h + (v % 4);
-                if (m < a.M && n < a.N) {
-                    float *y = a.Y + (int64_t)m * a.ldy + n;
-                    if (a.splits > 1)
-                        __hip_atomic_fetch_add(y, acc[mt][nt][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    else
-                        *y = acc[mt][nt][v];
+                for (int v = 0; v < 16; ++v) {
+                    const int m = m0 + wm * 32 * kMT + mt * 32 + 8 * (v / 4) + 4 * h + (v % 4);
+                    if (m < a.M && n < a.N) {
+                        float *y = a.Y + (int64_t)m * a.ldy + n;
+                        if (add)
+                            __hip_atomic_fetch_add(y, acc[mt][nt][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        else
+                            *y = acc[mt][nt][v];
+                    }
                 }
             }
-        }
+    };
+
+    // whole tiles, one round after another
+    for (int t = blockIdx.x; t < a.t1; t += gridDim.x) piece(t, 0, a.pairs, false);
+    // then the other R tiles, workgroup w taking slice w / R of tile
+    // t1 + w % R: pairs [pairs j / ways, pairs (j + 1) / ways)
+    const int R = a.tiles - a.t1;
+    if (a.ways > 0 && (int)blockIdx.x < R * a.ways) {
+        const int j = (int)blockIdx.x / R;
+        piece(a.t1 + (int)blockIdx.x % R, a.pairs * j / a.ways, a.pairs * (j + 1) / a.ways, true);
+    }
 }
 
-// Y[m][0..N) = 0 for m < M, ahead of a split launch (a kernel rather than a
-// memset, so that the call can be captured into a graph).
-__global__ __launch_bounds__(256) void zero_rows(float *Y, int64_t ldy, int32_t N, int32_t M)
+// Y = 0 over tiles [t1, tiles) (rows and columns past M and N left alone),
+// ahead of a launch whose workgroups add into them (a kernel rather than a
+// memset, so that the call can be captured into a graph).  Workgroup (x, y)
+// clears rows 4 x .. 4 x + 3 of tile t1 + y.
+__global__ __launch_bounds__(256) void zero_tiles(PfArgs a)
 {
-    const int64_t n = (int64_t)N * M;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-        Y[(i / N) * ldy + i % N] = 0.0f;
+    const int t = a.t1 + (int)blockIdx.y;
+    const int col = (t % a.tn) * kPfN + (int)threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = (t / a.tn) * kPfM + 4 * (int)blockIdx.x + i;
+        if (m < a.M && col < a.N) a.Y[(int64_t)m * a.ldy + col] = 0.0f;
+    }
 }
 
 bool set_prefill_attr()
@@ -315,26 +351,38 @@ pn_status pn_gemm_prefill(pn_type t, const void *W, int64_t N, int64_t K, const 
     a.M = (int32_t)M;
     a.S = (int32_t)(nb * 34);
     a.pairs = (int32_t)(nb / 2);
-    // One workgroup per CU (the two LDS stages take 102-118 KiB).  When the
-    // output tiles cannot fill the CUs, split K into as many slices as keep
-    // one round of workgroups, each slice at least 4 block pairs.
-    const int64_t tiles = ((N + kPfN - 1) / kPfN) * ((M + kPfM - 1) / kPfM);
-    int64_t splits = tiles >= device_cus() ? 1 : device_cus() / tiles;
-    if (splits > a.pairs / 4) splits = a.pairs / 4;
-    if (splits < 1) splits = 1;
-    a.splits = (int32_t)splits;
-    const dim3 grid((unsigned)((N + kPfN - 1) / kPfN), (unsigned)((M + kPfM - 1) / kPfM), (unsigned)splits);
+    // One workgroup per CU (the two LDS stages take 102-118 KiB): the tiles
+    // of whole rounds are dealt whole, and the R others are each shared by
+    // `ways` workgroups, as many as fit one round, at most 8 and with at
+    // least 4 block pairs each: the atomic adds of a shared tile cost about
+    // as much as computing a few of its pairs (on 256 CUs, 16 gate tiles
+    // shared 16 ways took 136 us, shared 8 ways less).
+    const int64_t G = device_cus();
+    const int64_t tn = (N + kPfN - 1) / kPfN, tiles = tn * ((M + kPfM - 1) / kPfM);
+    if (tiles > INT32_MAX) return PN_EUNSUPPORTED;
+    a.tn = (int32_t)tn;
+    a.tiles = (int32_t)tiles;
+    a.t1 = (int32_t)(tiles / G * G);
+    const int64_t R = tiles - a.t1;
+    int64_t ways = R > 0 ? G / R : 1;
+    if (ways > kPfMaxWays) ways = kPfMaxWays;
+    if (ways > a.pairs / 4) ways = a.pairs / 4;
+    if (ways < 2) {  // no tile is shared: the rest are dealt whole too
+        a.t1 = (int32_t)tiles;
+        ways = 0;
+    }
+    a.ways = (int32_t)ways;
+    const int64_t g2 = R * ways;
+    const int64_t grid = a.t1 > 0 ? (G < tiles ? G : tiles) : g2;
     const hipStream_t s = (hipStream_t)stream;
-    if (splits > 1) {
-        const int64_t n = N * M;
-        const int64_t blocks = (n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536;
-        hipLaunchKernelGGL(zero_rows, dim3((unsigned)blocks), dim3(256), 0, s, Y, ldy, (int32_t)N, (int32_t)M);
+    if (g2 > 0) {
+        hipLaunchKernelGGL(zero_tiles, dim3(kPfM / 4, (unsigned)(tiles - a.t1)), dim3(kPfN), 0, s, a);
         if (hipGetLastError() != hipSuccess) return PN_ELAUNCH;
     }
     if (t == PN_PN3T)
-        hipLaunchKernelGGL(gemm_prefill<0>, grid, dim3(kPfThreads), Pf<0>::LDS, s, a);
+        hipLaunchKernelGGL(gemm_prefill<0>, dim3((unsigned)grid), dim3(kPfThreads), Pf<0>::LDS, s, a);
     else
-        hipLaunchKernelGGL(gemm_prefill<1>, grid, dim3(kPfThreads), Pf<1>::LDS, s, a);
+        hipLaunchKernelGGL(gemm_prefill<1>, dim3((unsigned)grid), dim3(kPfThreads), Pf<1>::LDS, s, a);
     if (hipGetLastError() != hipSuccess) return PN_ELAUNCH;
     g_last_variant = kVarPrefill;
     return PN_OK;

@@ -4,7 +4,7 @@ product, within 1e-5 * sum|w x| for every (row of X, weight row)."""
 import numpy as np
 import pytest
 
-from gpu_util import assert_gemv_close, dev, say, sync
+from gpu_util import assert_bits_equal, assert_gemv_close, dev, say, sync
 
 torch = pytest.importorskip("torch")
 
@@ -111,8 +111,10 @@ def test_prefill_subnormal_activations(t):
 
 def test_prefill_layer_full_size():
     """Every product of one 27B-shaped layer (q, k, v, o, gate, up, down) with
-    a 512-token prompt chunk, as the benchmark runs it (k, v and o split K
-    over the CUs): every output against the oracle."""
+    a 512-token prompt chunk, as the benchmark runs it (on 256 CUs: gate and
+    up 272 tiles, one round dealt whole and 16 tiles' block pairs shared; q
+    96 tiles, o and down 80, k and v 16, all shared): every output against
+    the oracle."""
     m = 512
     g = np.random.default_rng(21)
     for name, t, n, k in synth.SWEEP_LAYER:
@@ -122,3 +124,37 @@ def test_prefill_layer_full_size():
         y = gpu_prefill(t, w, n, k, xm)
         y64, a = pnref.gemm_f64(t, w, n, k, xm)
         assert_gemv_close(y, y64, a, "prefill full size %s" % name)
+
+
+def cus():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+@pytest.mark.parametrize("case", ["one_over", "two_rounds_and_three", "two_m_tiles", "below"])
+def test_prefill_dealing(case):
+    """The tiles of whole rounds dealt whole and the rest's block pairs
+    shared (by two workgroups here: 8 or 10 pairs a tile, at least 4 a
+    piece): launches with one tile more than a round, two rounds and three
+    tiles, tiles over two M tiles, and fewer tiles than CUs; ragged last
+    tiles in N and M.  Every output against the oracle; the rows of tiles
+    dealt whole come out the same on a second run."""
+    G = cus()
+    t, n, k, m = {"one_over": ("pn3t", (G + 1) * 256 - 100, 1280, 1),
+                  "two_rounds_and_three": ("pn4t", (2 * G + 3) * 256, 1280, 1),
+                  "two_m_tiles": ("pn3t", (G // 2 + 1) * 256 - 7, 1280, 200),
+                  "below": ("pn4t", (G // 8) * 256 + 33, 1280, 130)}[case]
+    g = np.random.default_rng([77, n, k, m])
+    w = synth.random_blocks(g, t, n, k, unused_bits=True)
+    xm = synth.activation(g, k, m)
+    say("prefill dealing %s: %s N=%d K=%d M=%d on %d CUs" % (case, t, n, k, m, G))
+    y = gpu_prefill(t, w, n, k, xm)
+    y64, a = pnref.gemm_f64(t, w, n, k, xm)
+    assert_gemv_close(y, y64, a, "prefill dealing %s" % case)
+    tiles = ((n + 255) // 256) * ((m + 127) // 128)
+    whole = tiles // G * G
+    if whole:  # tiles [0, whole) in (M tile, N tile) order, N fastest
+        tn = (n + 255) // 256
+        y2 = gpu_prefill(t, w, n, k, xm)
+        for tile in range(whole):
+            r0, c0 = (tile // tn) * 128, (tile % tn) * 256
+            assert_bits_equal(y2[r0:r0 + 128, c0:c0 + 256], y[r0:r0 + 128, c0:c0 + 256], "tile %d dealt whole" % tile)
