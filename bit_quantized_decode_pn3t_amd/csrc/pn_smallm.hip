@@ -99,7 +99,7 @@ struct SmProb {
     int32_t tile0;     // first tile of this problem in the launch
     int32_t cb;        // blocks per activation chunk
     int32_t nchunks;
-    int32_t stride;    // LDS bytes per staged activation row (multiple of 256)
+    int32_t stride;    // LDS bytes per staged activation row (256 k + 32 for pn3t, 256 k + 48 for pn4t)
 };
 
 struct SmArgs {
@@ -110,16 +110,60 @@ struct SmArgs {
 };
 
 // LDS address of byte o of staged activation row m.  Rows are `stride` bytes
-// apart (a multiple of 256).  The XOR moves 32-byte (pn3t) or 16-byte (pn4t)
-// pieces inside a 256-byte window so that the distinct reads of one operand
-// load (up to 16 rows x 4 lane groups) spread over the banks as evenly as
-// their total size allows: pn3t reads 8 bytes at 40g + 8s, pn4t 16 bytes at
-// 32g + 16s.
+// apart: a multiple of 256 plus 32 (pn3t) or 48 (pn4t), so that the distinct
+// reads of one operand load (up to 16 rows x 4 lane groups; pn3t reads 8 or
+// 16 bytes at 40g + ..., pn4t 16 bytes at 32g + 16s) spread over the banks
+// as evenly as an XOR swizzle of the rows would spread them, while an
+// operand's address stays a per-lane base plus a constant.
 template <int TYPE>
 __device__ __forceinline__ uint32_t xoff(uint32_t m, uint32_t stride, uint32_t o)
 {
-    const uint32_t sw = TYPE == 0 ? ((m & 7u) << 5) : (((m & 1u) << 7) | ((m & 2u) << 3));
-    return m * stride + (o ^ sw);
+    return m * stride + o;
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>());
+        static_for<I + 1, N>(f);
+    }
+}
+
+// LDS reads issued where they stand (inline asm, so that the compiler cannot
+// sink them next to their use) and the wait that retires them, tied to the
+// registers they fill: every read must be retired before its registers die.
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_b64(uint32_t a)
+{
+    u32x2 r;
+    asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(OFF));
+    return r;
+}
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_b128(uint32_t a)
+{
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(OFF));
+    return r;
+}
+template <int OFF0, int OFF1>
+__device__ __forceinline__ u32x4 lds_2b64(uint32_t a)
+{
+    static_assert(OFF0 % 8 == 0 && OFF1 % 8 == 0 && OFF1 / 8 < 256, "ds_read2_b64 offsets");
+    u32x4 r;
+    asm volatile("ds_read2_b64 %0, %1 offset0:%2 offset1:%3" : "=v"(r) : "v"(a), "i"(OFF0 / 8), "i"(OFF1 / 8));
+    return r;
+}
+// X operands of one block as read (pn3t: 16 + 16 + 8 bytes, pn4t: 16 + 16)
+struct XOp {
+    u32x4 a, b;
+    u32x2 c;
+};
+template <int N>
+__device__ __forceinline__ void lgkm_wait(XOp &x)
+{
+    asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(x.a), "+v"(x.b), "+v"(x.c) : "i"(N) : "memory");
 }
 
 // Stage activation blocks [b0, b0 + nbc) of all M rows into LDS.  The loads
@@ -501,36 +545,44 @@ __global__ __launch_bounds__(kSmThreads) void gemm_stream(SmArgs args)
 // bytes of one row, sixteen rows per instruction) cap that kernel near 4 TB/s
 // even with its arithmetic taken out: each request carries 32 bytes and
 // every 128-byte line is requested four times.  Here a wave owns 16 rows (one
-// MFMA column group) and streams them a period at a time (8 blocks: 272
-// bytes, 17 aligned 16-byte chunks of each row) into an LDS stage by 16-byte
-// DMA (buffer_load_dwordx4 ... lds), which reads each row's period
-// contiguously; the lanes then read their words and scales in the operand
-// layout straight from the stage, so no ds_bpermute is needed, and the stage
-// is refilled with the next period while they compute.  Rows must be
-// whole periods (K a multiple of 640 for pn3t, 512 for pn4t) and 16-byte
-// aligned.  The activations are staged per workgroup as in gemm_stream, in
-// the LDS the ring leaves free; chunk boundaries fall on periods.
+// MFMA column group) and streams them a stage at a time (kDmPPS periods of 8
+// blocks: 272 bytes, 17 aligned 16-byte chunks of each row per period) into
+// LDS by 16-byte DMA (buffer_load_dwordx4 ... lds), which reads each row's
+// stage contiguously; the lanes then read their words and scales in the
+// operand layout straight from the stage, so no ds_bpermute is needed, and
+// the stage is refilled while they compute: with the tile's next stage, or
+// at its last stage with the next tile's first, so that a wave's loads run
+// on from tile to tile.  Rows must be whole periods (K a multiple of 640 for
+// pn3t, 512 for pn4t) and 16-byte aligned.  The activations are staged per
+// workgroup as in gemm_stream, in the LDS the ring leaves free; chunk
+// boundaries fall on stages.
 //
-// Stage layout: row r's period at byte 272 r (DMA slot 17 r + c holds its
-// chunk c).  In each block pair (68 bytes = 17 dwords D) the first block's
-// scale is the low half of D[0] and its word j is D[j..j+1] shifted by 16
-// bits; the second block's scale is the high half of D[8] and its word j is
-// D[9 + j].  Lane (gm, jm) takes row jm and the block's words 2gm, 2gm + 1,
-// the same k-group as gemm_stream's operand layout.
+// Stage layout: row r's periods at byte 272 kDmPPS r (DMA slot 17 kDmPPS r +
+// c holds its chunk c).  In each block pair (68 bytes = 17 dwords D) the
+// first block's scale is the low half of D[0] and its word j is D[j..j+1]
+// shifted by 16 bits; the second block's scale is the high half of D[8] and
+// its word j is D[9 + j].  Lane (gm, jm) takes row jm and the block's words
+// 2gm, 2gm + 1, the same k-group as gemm_stream's operand layout.
+//
+// Products: v_mfma_f32_16x16x32_f16, the lane's k-group holding 8 of a
+// block's k: pn4t 2 steps (its 16 codes), pn3t 3 steps (its 20 codes, then 4
+// zeros in both operands).  The X operands of a block are read from LDS one
+// block ahead of their products.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Waves per workgroup and ring stages per wave (measured on the M = 8 sweep):
-// 16 waves with one stage each (a wave reads its stage into registers and
-// refills it at once, so that one period is in flight while it computes;
-// four waves per SIMD hide each other's latencies) 2.41-2.51 ms; 8 waves
-// with two stages 2.66-2.68 ms, with one 2.60; 12 waves with one 2.63.
-// Three stages leave too little LDS for the activations (3.03 ms).
+// Waves per workgroup and periods per stage (measured on the M = 8 sweep;
+// one stage per wave: a wave reads its stage into registers and refills it
+// at once, so that one stage is in flight while it computes).  16 waves of
+// one-period stages: four waves per SIMD hide each other's latencies.  Two
+// periods a stage read faster (12 waves: 1.97 ms a token with the
+// arithmetic taken out, against 2.14 ms) but leave too little LDS for 16
+// waves, and with three waves per SIMD the arithmetic no longer hides behind
+// the loads (2.46 ms against 2.27 ms).  Earlier forms: 8 waves with two
+// one-period stages each 2.66-2.68 ms; three stages left too little LDS for
+// the activations (3.03 ms).
 #ifndef PN_SM_DMA_WAVES
 #define PN_SM_DMA_WAVES 16
-#endif
-#ifndef PN_SM_DMA_STAGES
-#define PN_SM_DMA_STAGES 1
 #endif
 // Tiles a workgroup takes per step of the grid stride: consecutive tiles
 // (usually of one problem) share one activation staging.  Measured on the
@@ -543,166 +595,256 @@ constexpr int kDmRows = 16;                              // rows per wave
 constexpr int kDmWaves = PN_SM_DMA_WAVES;                // waves per workgroup (one workgroup per CU)
 constexpr int kDmThreads = 64 * kDmWaves;
 constexpr int kDmTileRows = kDmWaves * kDmRows;          // rows per workgroup tile
-constexpr int kDmChunks = 17;                            // 16-byte chunks per row and period
-constexpr int kDmDma = (kDmRows * kDmChunks + 63) / 64;  // DMA instructions per stage (5)
-constexpr int kDmStage = 1024 * kDmDma;                  // LDS bytes per stage
-constexpr int kDmNS = PN_SM_DMA_STAGES;                  // stages per wave
-constexpr int kDmGroup = PN_SM_DMA_GROUP;                // consecutive tiles per grid-stride step
-constexpr int kDmRing = kDmWaves * kDmNS * kDmStage;     // 80 KiB
-constexpr int kDmLdsX = kSmLdsMax - kDmRing;             // activation chunk budget
-static_assert(kDmNS >= 1 && kDmNS <= 3 && kDmThreads <= 1024 && kDmRing < kSmLdsMax, "ring shape");
+#ifndef PN_SM_DMA_PPS
+#define PN_SM_DMA_PPS 1
+#endif
+constexpr int kDmPPS = PN_SM_DMA_PPS;                             // periods per stage
+constexpr int kDmChunks = 17 * kDmPPS;                            // 16-byte chunks per row and stage
+constexpr int kDmDma = (kDmRows * kDmChunks + 63) / 64;           // DMA instructions per stage
+constexpr int kDmStage = 16 * kDmRows * kDmChunks;                // LDS bytes per stage (4,352 per period)
+constexpr int kDmLast = kDmRows * kDmChunks - 64 * (kDmDma - 1);  // lanes of the last DMA instruction
+constexpr int kDmGroup = PN_SM_DMA_GROUP;                         // consecutive tiles per grid-stride step
+constexpr int kDmRing = kDmWaves * kDmStage;                      // 68 KiB
+constexpr int kDmLdsX = kSmLdsMax - kDmRing;                      // activation chunk budget
+static_assert(kDmPPS >= 1 && kDmPPS <= 2 && kDmThreads <= 1024 && kDmRing < kSmLdsMax, "ring shape");
 
+// Where one wave's rows of a tile are: the resource covering its valid
+// rows (rows past N read zeros and are not stored), the row bytes and the
+// number of periods and stages.
+struct DmSrc {
+    __amdgpu_buffer_rsrc_t rs;
+    int32_t S, nper, nst, valid;
+};
+
+__device__ __forceinline__ DmSrc dm_src(const SmProb &p, int row0)
+{
+    DmSrc d;
+    const int nb = uniform(p.nb);
+    d.S = 34 * nb;
+    d.nper = nb >> 3;
+    d.nst = (d.nper + kDmPPS - 1) / kDmPPS;
+    d.valid = uniform(p.N - row0 < kDmRows ? p.N - row0 : kDmRows);  // <= 0: no rows
+    d.rs = make_rsrc(uniform_ptr(p.W + (size_t)(d.valid > 0 ? row0 : 0) * d.S),
+                     d.valid > 0 ? (uint32_t)d.valid * (uint32_t)d.S : 0u);
+    return d;
+}
+
+// Stage s of a tile into `st`: periods kDmPPS s .. of the wave's rows; the
+// chunks of periods past the row's end read nothing.  (rr, cc): the lane's
+// row and chunk in each DMA instruction's slot.
+__device__ __forceinline__ void dm_issue(const DmSrc &d, int s, uint8_t *st, const uint32_t (&rr)[kDmDma],
+                                         const uint32_t (&cc)[kDmDma], int lane)
+{
+    const uint32_t lim = 17u * (uint32_t)(d.nper - kDmPPS * s);  // chunks left in the row
+#pragma unroll
+    for (int i = 0; i < kDmDma; ++i) {
+        const uint32_t o = rr[i] < (uint32_t)kDmRows && (kDmPPS == 1 || cc[i] < lim)
+                               ? rr[i] * (uint32_t)d.S + 16u * cc[i]
+                               : 0x80000000u;
+        if (i < kDmDma - 1 || lane < kDmLast)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rs, (lds_void *)(st + 1024 * i), 16, (int)o, 272 * kDmPPS * s, 0,
+                                                     0);
+    }
+}
+
+// One tile of one wave.  Its stage 0 was issued by the caller; while its last
+// stage is computed, the next tile's stage 0 (nx, when has_next) is already
+// in flight.
 template <int TYPE>
-__device__ __forceinline__ void dm_tile(const SmProb &p, int row0, uint8_t *lds, uint8_t *ring)
+__device__ __forceinline__ void dm_tile(const SmProb &p, int row0, const DmSrc &d, const DmSrc &nx, bool has_next,
+                                        uint8_t *lds, uint8_t *ring, const uint32_t (&rr)[kDmDma],
+                                        const uint32_t (&cc)[kDmDma])
 {
     constexpr int P = Unpack<TYPE>::kPairs;
     const int lane = threadIdx.x & 63;
     const int jm = lane & 15, gm = lane >> 4;  // operand layout: row jm, k-group gm
     const int nb = uniform(p.nb), cb = uniform(p.cb), M = uniform(p.M);
-    const int nper = nb >> 3;
+    const int nper = d.nper, nst = d.nst;
     const uint32_t stride = (uint32_t)uniform(p.stride);
-    const int S = 34 * nb;
-    const int valid = uniform(p.N - row0 < kDmRows ? p.N - row0 : kDmRows);  // <= 0: no rows
-    // rows past N read zeros (offsets past the resource) and are not stored
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(uniform_ptr(p.W + (size_t)(valid > 0 ? row0 : 0) * S),
-                                                valid > 0 ? (uint32_t)valid * (uint32_t)S : 0u);
-    uint32_t vo[kDmDma];
-#pragma unroll
-    for (int i = 0; i < kDmDma; ++i) {
-        const uint32_t q = 64u * i + (uint32_t)lane, r = q / kDmChunks, c = q - kDmChunks * r;
-        vo[i] = r < (uint32_t)kDmRows ? r * (uint32_t)S + 16u * c : 0x80000000u;
-    }
     const uint32_t ma = jm < M ? (uint32_t)jm : 0u;  // A row; rows >= M are discarded
     float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto issue = [&](int per) {
-        uint8_t *st = ring + (per % kDmNS) * kDmStage;
-#pragma unroll
-        for (int i = 0; i < kDmDma; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(st + 1024 * i), 16, (int)vo[i], 272 * per, 0, 0);
-    };
-
     int cbase = 0;                      // first block of the staged chunk
     int cnext = cb < nb ? cb : nb + 1;  // block at which the next chunk is staged
-    for (int q = 0; q < kDmNS && q < nper; ++q) issue(q);
-    // One period.  LATER: stages issued after this one (a compile-time count,
-    // so that the wait is one instruction).
-    auto period = [&](int per, auto later_c) {
-        constexpr int LATER = decltype(later_c)::value;
-        const int b0 = 8 * per;
+    for (int s = 0; s < nst; ++s) {
+        const int b0 = 8 * kDmPPS * s;
+        const int nv = nper - kDmPPS * s < kDmPPS ? nper - kDmPPS * s : kDmPPS;  // periods in this stage
         if (b0 == cnext) {
-            // every wave of the workgroup is on this problem and period
+            // every wave of the workgroup is on this problem and stage
             __syncthreads();
             stage_chunk<TYPE, kDmThreads>(p, b0, nb - b0 < cb ? nb - b0 : cb, lds);
             // (the staging loads are younger than the ring's DMA, so the ring
             // has landed too; saying so on every path keeps the compiler from
-            // draining the ring at every period for loads it thinks pending)
+            // draining the ring at every stage for loads it thinks pending)
             __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
             __syncthreads();
             cbase = b0;
             cnext = b0 + cb;
         }
-        __builtin_amdgcn_s_waitcnt(0x0f70 | (LATER * kDmDma));  // vmcnt(LATER * kDmDma)
-        // the lane's words and scales of the period: per block pair, D[2gm ..
-        // 2gm + 2], D[9 + 2gm], D[10 + 2gm], D[0], D[8]
-        const uint8_t *st = ring + (per % kDmNS) * kDmStage;
-        const uint32_t *rw = (const uint32_t *)(st + 272 * jm);
-        uint32_t wa[4][3], wb[4][2], sa[4], sb[4];
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the stage (and the last tile's stores)
+        // the lane's words and scales of each period: per block pair,
+        // D[2gm .. 2gm + 2], D[9 + 2gm], D[10 + 2gm], D[0], D[8]
+        const uint32_t *rw = (const uint32_t *)(ring + 272 * kDmPPS * jm);
+        uint32_t wa[kDmPPS][4][3], wb[kDmPPS][4][2], sa[kDmPPS][4], sb[kDmPPS][4];
 #pragma unroll
-        for (int bp = 0; bp < 4; ++bp) {
+        for (int pp = 0; pp < kDmPPS; ++pp)
 #pragma unroll
-            for (int j = 0; j < 3; ++j) wa[bp][j] = rw[17 * bp + 2 * gm + j];
-            wb[bp][0] = rw[17 * bp + 9 + 2 * gm];
-            wb[bp][1] = rw[17 * bp + 10 + 2 * gm];
-            sa[bp] = rw[17 * bp];
-            sb[bp] = rw[17 * bp + 8];
-        }
-        // the stage is refilled once its reads have landed
+            for (int bp = 0; bp < 4; ++bp) {
+                const int o = 68 * pp + 17 * bp;
+#pragma unroll
+                for (int j = 0; j < 3; ++j) wa[pp][bp][j] = rw[o + 2 * gm + j];
+                wb[pp][bp][0] = rw[o + 9 + 2 * gm];
+                wb[pp][bp][1] = rw[o + 10 + 2 * gm];
+                sa[pp][bp] = rw[o];
+                sb[pp][bp] = rw[o + 8];
+            }
+        // the stage is refilled once its reads have landed: with this tile's
+        // next stage, or the next tile's first
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
         asm volatile("" ::: "memory");
-        if (per + kDmNS < nper) issue(per + kDmNS);
+        if (s + 1 < nst)
+            dm_issue(d, s + 1, ring, rr, cc, lane);
+        else if (has_next)
+            dm_issue(nx, 0, ring, rr, cc, lane);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            const int bp = b >> 1;
+        constexpr uint32_t kBB = TYPE == 0 ? 160u : 128u;  // X bytes per block and row
+        const uint32_t xs = (uint32_t)(size_t)(lds_void *)(lds + ma * stride + (TYPE == 0 ? 40u : 32u) * (uint32_t)gm +
+                                                          kBB * (uint32_t)(b0 - cbase));
+        constexpr int NQ = 8 * kDmPPS;         // blocks of a stage
+        constexpr int XR = TYPE == 0 ? 3 : 2;  // X read instructions per block
+        // X operands of block q (the lane's 40 or 32 bytes), read one block
+        // ahead straight into the registers the MFMAs take (nothing may copy
+        // them before the wait that retires the reads)
+        auto xread = [&](auto qc, XOp &x) {
+            constexpr int q = decltype(qc)::value, o = (int)kBB * (q % 8);
+            const uint32_t a = xs + 8u * kBB * (uint32_t)(q / 8);
+            if constexpr (TYPE == 0) {
+                x.a = lds_2b64<o, o + 8>(a);
+                x.b = lds_2b64<o + 16, o + 24>(a);
+                x.c = lds_b64<o + 32>(a);
+            } else {
+                x.a = lds_b128<o>(a);
+                x.b = lds_b128<o + 16>(a);
+                x.c = (u32x2){0u, 0u};
+            }
+        };
+        XOp xa, xb;
+        xread(std::integral_constant<int, 0>(), xa);
+        auto block = [&](auto qc) {
+            constexpr int q = decltype(qc)::value, pp = q / 8, b = q % 8, bp = b >> 1;
+            XOp &xc = q % 2 == 0 ? xa : xb;
+            XOp &xn = q % 2 == 0 ? xb : xa;
+            if constexpr (q + 1 < NQ) {
+                xread(std::integral_constant<int, q + 1>(), xn);
+                lgkm_wait<XR>(xc);
+            } else {
+                lgkm_wait<0>(xc);
+            }
             uint32_t w0, w1, sc;
             if (b & 1) {
-                w0 = wb[bp][0];
-                w1 = wb[bp][1];
-                sc = sb[bp] >> 16;
+                w0 = wb[pp][bp][0];
+                w1 = wb[pp][bp][1];
+                sc = sb[pp][bp] >> 16;
             } else {
-                w0 = __builtin_amdgcn_alignbit(wa[bp][1], wa[bp][0], 16);
-                w1 = __builtin_amdgcn_alignbit(wa[bp][2], wa[bp][1], 16);
-                sc = sa[bp] & 0xffffu;
+                w0 = __builtin_amdgcn_alignbit(wa[pp][bp][1], wa[pp][bp][0], 16);
+                w1 = __builtin_amdgcn_alignbit(wa[pp][bp][2], wa[pp][bp][1], 16);
+                sc = sa[pp][bp] & 0xffffu;
             }
             half2_t u[P], v[P];
             Unpack<TYPE>::run(w0, u);
             Unpack<TYPE>::run(w1, v);
             const float d = half_bits_to_float(sc);
-            const uint32_t bl = (uint32_t)(b0 + b - cbase);
             float4_t D;
+            const half8_t a0 = __builtin_bit_cast(half8_t, xc.a), a1 = __builtin_bit_cast(half8_t, xc.b);
             if constexpr (TYPE == 0) {
-                half4_t a[5];
-#pragma unroll
-                for (int s5 = 0; s5 < 5; ++s5)
-                    a[s5] = __builtin_bit_cast(
-                        half4_t, *(const u32x2 *)(lds + xoff<0>(ma, stride, 160u * bl + 40u * gm + 8u * s5)));
-                // pairs 0..4 from word 2gm, 5..9 from word 2gm + 1; step s takes pairs 2s, 2s + 1
-                D = __builtin_amdgcn_mfma_f32_16x16x16f16(a[0], __builtin_shufflevector(u[0], u[1], 0, 1, 2, 3),
-                                                          (float4_t){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-                D = __builtin_amdgcn_mfma_f32_16x16x16f16(a[1], __builtin_shufflevector(u[2], u[3], 0, 1, 2, 3), D, 0, 0, 0);
-                D = __builtin_amdgcn_mfma_f32_16x16x16f16(a[2], __builtin_shufflevector(u[4], v[0], 0, 1, 2, 3), D, 0, 0, 0);
-                D = __builtin_amdgcn_mfma_f32_16x16x16f16(a[3], __builtin_shufflevector(v[1], v[2], 0, 1, 2, 3), D, 0, 0, 0);
-                D = __builtin_amdgcn_mfma_f32_16x16x16f16(a[4], __builtin_shufflevector(v[3], v[4], 0, 1, 2, 3), D, 0, 0, 0);
-            } else {
-                half8_t a[2];
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2)
-                    a[s2] = __builtin_bit_cast(
-                        half8_t, *(const u32x4 *)(lds + xoff<1>(ma, stride, 128u * bl + 32u * gm + 16u * s2)));
+                // k-steps of 32: the lane's codes 0-7, 8-15 and 16-19 (then four zeros) of its 20
+                const half8_t a2 = __builtin_bit_cast(half8_t, (u32x4){xc.c[0], xc.c[1], 0u, 0u});
+                const half2_t z = {0.0f16, 0.0f16};
                 const half8_t b0v = __builtin_shufflevector(__builtin_shufflevector(u[0], u[1], 0, 1, 2, 3),
-                                                            __builtin_shufflevector(u[2], u[3], 0, 1, 2, 3), 0, 1,
-                                                            2, 3, 4, 5, 6, 7);
+                                                            __builtin_shufflevector(u[2], u[3], 0, 1, 2, 3), 0, 1, 2,
+                                                            3, 4, 5, 6, 7);
+                const half8_t b1v = __builtin_shufflevector(__builtin_shufflevector(u[4], v[0], 0, 1, 2, 3),
+                                                            __builtin_shufflevector(v[1], v[2], 0, 1, 2, 3), 0, 1, 2,
+                                                            3, 4, 5, 6, 7);
+                const half8_t b2v = __builtin_shufflevector(__builtin_shufflevector(v[3], v[4], 0, 1, 2, 3),
+                                                            __builtin_shufflevector(z, z, 0, 1, 2, 3), 0, 1, 2, 3, 4,
+                                                            5, 6, 7);
+                D = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0v, (float4_t){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                D = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1v, D, 0, 0, 0);
+                D = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2, b2v, D, 0, 0, 0);
+            } else {
+                const half8_t b0v = __builtin_shufflevector(__builtin_shufflevector(u[0], u[1], 0, 1, 2, 3),
+                                                            __builtin_shufflevector(u[2], u[3], 0, 1, 2, 3), 0, 1, 2,
+                                                            3, 4, 5, 6, 7);
                 const half8_t b1v = __builtin_shufflevector(__builtin_shufflevector(v[0], v[1], 0, 1, 2, 3),
-                                                            __builtin_shufflevector(v[2], v[3], 0, 1, 2, 3), 0, 1,
-                                                            2, 3, 4, 5, 6, 7);
-                D = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], b0v, (float4_t){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-                D = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[1], b1v, D, 0, 0, 0);
+                                                            __builtin_shufflevector(v[2], v[3], 0, 1, 2, 3), 0, 1, 2,
+                                                            3, 4, 5, 6, 7);
+                D = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0v, (float4_t){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                D = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1v, D, 0, 0, 0);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(D[i], d, acc[i]);
-        }
-    };
-    int per = 0;
-    for (; per + kDmNS - 1 < nper; ++per) period(per, std::integral_constant<int, kDmNS - 1>());
-    if constexpr (kDmNS >= 3)
-        if (per + 1 < nper) period(per++, std::integral_constant<int, 1>());
-    if (per < nper) period(per, std::integral_constant<int, 0>());
+        };
+        // periods past the row's end (the last stage of a row may hold fewer)
+        // are skipped; the X read issued ahead for the first of them is retired
+        static_for<0, kDmPPS>([&](auto pc) {
+            constexpr int pp = decltype(pc)::value;
+            if (pp == 0 || nv > pp)
+                static_for<8 * pp, 8 * pp + 8>(block);
+            else if (nv == pp)
+                lgkm_wait<0>(xa);
+        });
+    }
     // lane (jm, gm) holds D[m = 4gm + i][row jm]
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int m = 4 * gm + i;
-        if (m < M && jm < valid) p.Y[p.ldy * m + row0 + jm] = acc[i];
+        if (m < M && jm < d.valid) p.Y[p.ldy * m + row0 + jm] = acc[i];
     }
-    // no DMA or store may be outstanding when the next tile reuses the ring
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 }
 
 // Workgroups take tiles (kDmWaves x 16 rows of one problem) in a grid
 // stride, as gemm_stream does; the ring sits above the activation chunk.
+// A wave's stages run on from one tile into the next without draining.
 __global__ __launch_bounds__(kDmThreads) void gemm_rows(SmArgs args)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int wave = uniform(threadIdx.x >> 6);
-    uint8_t *ring = lds + kDmLdsX + wave * kDmNS * kDmStage;
-    int i = 0, next0 = -1, staged = -1;
-    SmProb p;
+    const int lane = threadIdx.x & 63;
+    uint8_t *ring = lds + kDmLdsX + wave * kDmStage;
+    uint32_t rr[kDmDma], cc[kDmDma];
+#pragma unroll
+    for (int i = 0; i < kDmDma; ++i) {
+        const uint32_t q = 64u * i + (uint32_t)lane;
+        rr[i] = q / kDmChunks;
+        cc[i] = q - kDmChunks * rr[i];
+    }
     // kDmGroup consecutive tiles per step of the grid stride: the activations
     // staged for a problem serve all of its tiles in the group
     const int groups = (args.total_tiles + kDmGroup - 1) / kDmGroup;
-    for (int gi = blockIdx.x; gi < groups; gi += gridDim.x)
-    for (int tile = gi * kDmGroup; tile < (gi + 1) * kDmGroup && tile < args.total_tiles; ++tile) {
-        if (tile >= next0) sm_next_problem(args, tile, i, next0, p);
+    auto tile_at = [&](int k) {  // the workgroup's k-th tile, or -1
+        const int g = (int)blockIdx.x + (k / kDmGroup) * (int)gridDim.x, t = g * kDmGroup + k % kDmGroup;
+        return g < groups && t < args.total_tiles ? t : -1;
+    };
+    int t = tile_at(0);
+    if (t < 0) return;
+    int i = 0, next0 = -1, staged = -1;
+    SmProb p;
+    sm_next_problem(args, t, i, next0, p);
+    int row0 = ((t - p.tile0) * kDmWaves + wave) * kDmRows;
+    DmSrc d = dm_src(p, row0);
+    dm_issue(d, 0, ring, rr, cc, lane);
+    for (int k = 0;; ++k) {
+        // the next tile, looked up ahead so that its first stage can be issued early
+        const int tn = tile_at(k + 1);
+        SmProb pn = p;
+        int in = i, nn = next0, rn = 0;
+        DmSrc dn = d;
+        if (tn >= 0) {
+            if (tn >= nn) sm_next_problem(args, tn, in, nn, pn);
+            rn = ((tn - pn.tile0) * kDmWaves + wave) * kDmRows;
+            dn = dm_src(pn, rn);
+        }
         if (p.nchunks > 1 || staged != i) {
             const int nbc = p.nb < p.cb ? p.nb : p.cb;
             __syncthreads();
@@ -714,12 +856,19 @@ __global__ __launch_bounds__(kDmThreads) void gemm_rows(SmArgs args)
             __syncthreads();
         }
         staged = p.nchunks > 1 ? -1 : i;
-        const int row0 = ((tile - p.tile0) * kDmWaves + wave) * kDmRows;
         if (p.type == 0)
-            dm_tile<0>(p, row0, lds, ring);
+            dm_tile<0>(p, row0, d, dn, tn >= 0, lds, ring, rr, cc);
         else
-            dm_tile<1>(p, row0, lds, ring);
+            dm_tile<1>(p, row0, d, dn, tn >= 0, lds, ring, rr, cc);
+        if (tn < 0) break;
+        p = pn;
+        i = in;
+        next0 = nn;
+        row0 = rn;
+        d = dn;
     }
+    // no DMA or store may be outstanding when the wave ends
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 }
 
 // ---------------------------------------------------------------------------
@@ -780,7 +929,8 @@ bool sm_dma_ok(int t, const void *W, int64_t K, bool mfma)
 // Fill an SmProb for one problem (validated) and choose its activation
 // chunking: the fewest chunks of whole blocks whose M staged rows fit the LDS
 // budget, equal in size up to U blocks (every boundary a multiple of U), or
-// up to periods for gemm_rows (dma), whose ring takes part of the LDS.
+// up to stages for gemm_rows (dma), whose ring takes part of the LDS.  Rows are
+// padded to 32 or 48 bytes past a multiple of 256 (xoff).
 pn_status sm_make(int t, const void *W, int64_t N, int64_t K, const void *X, int64_t ldx, int M, float *Y,
                   int64_t ldy, bool mfma, bool dma, SmProb &p)
 {
@@ -793,13 +943,13 @@ pn_status sm_make(int t, const void *W, int64_t N, int64_t K, const void *X, int
     const int64_t nb = K / wpb(t);
     if (nb * 34 * kWaveRows > INT32_MAX) return PN_EUNSUPPORTED;  // per-wave offsets are 32-bit
     const int64_t bytes_per_block = (int64_t)wpb(t) * 2;              // staged bytes per block and row
-    const int64_t unit = dma ? 8 : kSmU;  // chunk boundaries at multiples of this many blocks
+    const int64_t unit = dma ? 8 * kDmPPS : kSmU;  // chunk boundaries at multiples of this many blocks
     const int64_t budget = dma ? kDmLdsX : mfma ? kSmLdsMax : kSmLdsValu;
     int64_t nchunks = 1, cb = nb, stride = 0;
     for (;; ++nchunks) {
         cb = (nb + nchunks - 1) / nchunks;
         if (cb < nb) cb = (cb + unit - 1) / unit * unit;
-        stride = (cb * bytes_per_block + 255) / 256 * 256;
+        stride = (cb * bytes_per_block + 255) / 256 * 256 + (t == 0 ? 32 : 48);
         if (stride * M <= budget) break;
         if (cb <= unit) return PN_EUNSUPPORTED;
     }
