@@ -24,7 +24,19 @@ wrong sums that way.  The shipped MFMA kernels start every block's chain
 from a zero accumulator and keep one shape per chain; the check below walks
 the control-flow graph of each compiled kernel backwards from every
 accumulating MFMA and fails on a different-shape MFMA result reached within
-5 wait states."""
+5 wait states.
+
+LDS reads issued from inline asm: the small-M DMA kernel reads each block's
+activation operands from LDS one block ahead of their use, with inline
+ds_read instructions the compiler does not know to be loads, each retired by
+an s_waitcnt lgkmcnt tied to the registers it fills.  The compiler may
+still copy or overwrite those registers before the wait if the asm output
+is not the very register the consumer takes (a first form assembled a
+128-bit operand from two 64-bit reads that way, and its pn3t products came
+out as NaN).  The check tracks, over the control-flow graph, the LDS reads
+possibly still outstanding (LDS operations complete in order, so an
+lgkmcnt(N) retires every read with at least N younger LDS reads) and fails
+on any instruction that touches their registers first."""
 import os
 import re
 import shutil
@@ -351,3 +363,136 @@ def test_no_cache_maintenance(tmp_path, src):
     assert "s_endpgm" in asm
     bad = [l.strip() for l in asm.splitlines() if re.match(r"\s*buffer_(wbl2|inv)\b", l)]
     assert bad == [], bad
+
+
+LDS_RETURNS = ("ds_read", "ds_bpermute", "ds_permute", "ds_swizzle")
+
+
+def _lds_returns(op):
+    return op.startswith(LDS_RETURNS) or (op.startswith("ds_") and "_rtn" in op)
+
+
+def find_lds_use_before_wait(asm, cap=64):
+    """Instructions that read or write a register an LDS read may still be
+    filling, on some path (forward dataflow over the control-flow graph; the
+    state maps each read to the fewest younger LDS reads issued after it on
+    any path reaching the point)."""
+    blocks, labels, succ = _blocks(asm)
+    entry = [None] * len(blocks)
+    entry[0] = {}
+    work = [0]
+    found = set()
+    # every function's first block is an entry too
+    for bi, lab in enumerate(labels):
+        if lab and not lab.startswith(".") and entry[bi] is None:
+            entry[bi] = {}
+            work.append(bi)
+
+    def step(state, bi, record):
+        st = dict(state)
+        for ii, line in enumerate(blocks[bi]):
+            op, args = _split(line)
+            if op == "s_waitcnt":
+                m = re.search(r"lgkmcnt\((\d+)\)", line)
+                if m:
+                    n = int(m.group(1))
+                    st = {k: v for k, v in st.items() if v[0] < n}
+                continue
+            regs = set()
+            for t in args:
+                regs |= _regs2(t.split()[0]) if t else set()
+            for key, (newer, dst) in st.items():
+                if dst & regs and record:
+                    found.add("%s touches the registers of %s before its wait" % (line, key[2]))
+            if _lds_returns(op) and args:
+                st = {k: (min(v[0] + 1, cap), v[1]) for k, v in st.items()}
+                st[(bi, ii, line)] = (0, _regs2(args[0].split()[0]))
+        return st
+
+    while work:
+        bi = work.pop()
+        out = step(entry[bi], bi, False)
+        for sj in succ[bi]:
+            cur = entry[sj]
+            if cur is None:
+                new = dict(out)
+            else:
+                new = dict(cur)
+                for k, v in out.items():
+                    new[k] = (min(v[0], new[k][0]), v[1]) if k in new else v
+            if new != cur:
+                entry[sj] = new
+                work.append(sj)
+    for bi in range(len(blocks)):
+        if entry[bi] is not None:
+            step(entry[bi], bi, True)
+    return sorted(found)
+
+
+def test_lds_wait_checker_flags_planted_uses():
+    planted = """
+_kernel:
+    ds_read_b64 v[2:3], v10 offset:0
+    ds_read_b64 v[4:5], v10 offset:8
+    v_mov_b32_e32 v20, v2
+    s_waitcnt lgkmcnt(1)
+    v_mov_b32_e32 v21, v2
+    v_mov_b32_e32 v22, v4
+    s_waitcnt lgkmcnt(0)
+    ds_read2_b64 v[30:33], v10 offset0:2 offset1:3
+    s_cbranch_scc1 .LBB0_2
+    v_add_f32_e32 v40, v41, v42
+    s_waitcnt lgkmcnt(0)
+.LBB0_2:
+    v_mov_b32_e32 v31, 0
+    s_waitcnt lgkmcnt(0)
+    v_mov_b32_e32 v32, 0
+    s_endpgm
+"""
+    got = find_lds_use_before_wait(planted)
+    # v20 <- v2 before any wait; v22 <- v4 after lgkmcnt(1) (the younger read
+    # may still be pending); v31 written at the join, where the branch taken
+    # skipped the wait; not v21 <- v2 (retired by lgkmcnt(1)), not v32
+    assert len(got) == 3, got
+    assert any("v20, v2 " in g or g.startswith("v_mov_b32_e32 v20, v2") for g in got), got
+    assert any(g.startswith("v_mov_b32_e32 v22, v4") for g in got), got
+    assert any(g.startswith("v_mov_b32_e32 v31, 0") for g in got), got
+
+
+COPY_SNIPPET = r"""
+#include <hip/hip_runtime.h>
+typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u2 rd(unsigned a)
+{
+    u2 r;
+    asm volatile("ds_read_b64 %0, %1" : "=v"(r) : "v"(a));
+    return r;
+}
+__global__ void copy_before_wait(u4 *out)
+{
+    extern __shared__ unsigned lds[];
+    const unsigned a = (unsigned)(size_t)(__attribute__((address_space(3))) void *)(lds + 4 * threadIdx.x);
+    const u2 r0 = rd(a), r1 = rd(a + 8);
+    u4 x = {r0[1], r1[0], r0[0], r1[1]};
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x) :: "memory");
+    out[threadIdx.x] = x;
+}
+"""
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None, reason="no hipcc")
+def test_lds_wait_checker_catches_a_copy_before_the_wait(tmp_path):
+    """Two asm reads whose results are rearranged into one operand before the
+    tied wait: the compiler copies the registers before the data is in."""
+    src = tmp_path / "copy.hip"
+    src.write_text(COPY_SNIPPET)
+    asm = _compile(tmp_path, src, "copy")
+    assert find_lds_use_before_wait(asm) != []
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None, reason="no hipcc")
+def test_small_m_kernels_wait_for_their_lds_reads(tmp_path):
+    asm = _compile(tmp_path, os.path.join(os.path.dirname(SRC), "pn_smallm.hip"), "pn_smallm.hip")
+    assert len(re.findall(r"^\s*ds_read2_b64", asm, re.M)) >= 16  # the read-ahead operands are there
+    assert find_lds_use_before_wait(asm) == []
