@@ -123,6 +123,7 @@ constexpr bool kSkipIdle = kNS == 1;
 constexpr int kRing = kRWaves * kNS * kStage;  // 155,648 bytes of LDS (147,456 without the boundary region)
 constexpr int kMinTilesPerCu = 32;            // below this "auto" uses gemv_stream
 constexpr int kPools = 16;                    // tile pools of a group launch
+constexpr uint32_t kPoolChunk = 64;           // consecutive tiles a pool is dealt at a time
 constexpr int kCounterStride = 1024;          // uint32s between pool counters (4 KiB)
 static_assert(kPools <= 32 && (kPools & (kPools - 1)) == 0, "pools: a power of two, one lane each");
 
@@ -267,11 +268,14 @@ __device__ __forceinline__ void period_dot(const uint32_t (&D)[68], const u32x4 
 // (up to 15 % apart on the sweep), so a static split leaves the fast ones
 // idle at the end.  One counter for the whole device would serialize the
 // grabs (device-scope atomics on one address, tens of ns each), so the
-// launch's tiles are dealt round-robin into kPools pools, one per half XCD,
-// each with its own counter; a wave takes tiles from its home pool and,
-// once that is empty, reads all the counters at once (one atomic add of
-// zero per lane) and moves to a pool with tiles left, or ends when none has
-// any.  (Trying the pools one by one cost a step per empty pool at the end
+// launch's tiles are dealt into kPools pools, one per half XCD, each with its
+// own counter: chunks of kPoolChunk consecutive tiles in turn, so that a
+// wave's next tiles are usually its last one's neighbours in memory (one
+// tile at a time, 16 tiles apart, ran the sweep 1 % slower; chunks of 1,024
+// and more leave long tiles to the end).  A wave takes tiles from its home
+// pool and, once that is empty, reads all the counters at once (one atomic
+// add of zero per lane) and moves to a pool with tiles left, or ends when
+// none has any.  (Trying the pools one by one cost a step per empty pool at the end
 // of every launch.)  The grab for a wave's next tile is issued at the start
 // of the step after it moved to a new tile, and read when it moves again,
 // at least one step later; so is the counter read.
@@ -349,24 +353,32 @@ __device__ __forceinline__ void wait_stage_and(uint32_t &k)
 }
 
 // Group launches: take the result of the outstanding grab or counter read
-// (readable: the caller has waited).  Index k of pool p is tile p + kPools k
-// of the launch, so pool p has tiles left while p + kPools k < tiles.  A
+// (readable: the caller has waited).  Index k of pool p is tile
+// pool_tile(p, k) of the launch, and pool p has tiles left while that is
+// below the launch's tile count (pool_tile grows with k).  A
 // grab that found its pool empty reads every counter; the read picks the
 // first pool with tiles left at or after the wave's own starting point (so
 // that the waves of an emptied pool spread over the others) and grabs from
 // it, or ends the wave.  Every grab and read moves the wave on: a pool's
 // counter only grows, so the wave ends after finitely many.
+// Index k of pool p: tile (k / C) kPools C + p C + k % C of the launch, C =
+// kPoolChunk.
+__device__ __forceinline__ uint32_t pool_tile(uint32_t p, uint32_t k)
+{
+    return (k / kPoolChunk) * (kPools * kPoolChunk) + p * kPoolChunk + k % kPoolChunk;
+}
+
 __device__ __forceinline__ void next_tile(Cursor &c, const RArgs &a, int lane, uint32_t &gv)
 {
     if (c.state == kScan) {
-        const bool open = lane < kPools && (uint32_t)lane + (uint32_t)kPools * gv < (uint32_t)a.total_tiles;
+        const bool open = lane < kPools && pool_tile((uint32_t)lane, gv) < (uint32_t)a.total_tiles;
         const uint32_t m = (uint32_t)__builtin_amdgcn_ballot_w64(open) & ((1u << kPools) - 1u);
         const uint32_t s = (uint32_t)c.rot;
         const uint32_t rm = ((m >> s) | (m << (kPools - s))) & ((1u << kPools) - 1u);  // pool s at bit 0
         c.pool = m != 0 ? (int32_t)(((uint32_t)__builtin_ctz(rm | (1u << kPools)) + s) & (uint32_t)(kPools - 1)) : c.pool;
         c.state = m != 0 ? kIdle : kDone;
     } else {
-        const uint32_t t = (uint32_t)c.pool + (uint32_t)kPools * (uint32_t)uniform((int32_t)gv);
+        const uint32_t t = pool_tile((uint32_t)c.pool, (uint32_t)uniform((int32_t)gv));
         if (t < (uint32_t)a.total_tiles) {
             const uint32_t e = a.lut[t];
             c.pi = (int32_t)(e >> 20);
@@ -852,8 +864,8 @@ pn_status pn::host::rows_group_create(const pn_gemv_desc *descs, int count, pn_g
     }
     // The plan: problems, the launch's tiles in the order they are handed out
     // (longest first, so that the last tiles of a run are short ones; pool p
-    // takes every kPools-th of them from p), and the pools' counters and the
-    // count of finished waves, 4 KiB apart.
+    // takes chunks p, p + kPools, ... of kPoolChunk of them), and the pools'
+    // counters and the count of finished waves, 4 KiB apart.
     const size_t tbytes = sizeof(RProb) * (size_t)count;
     const size_t lbytes = sizeof(uint32_t) * (size_t)total;
     const size_t cbytes = sizeof(uint32_t) * kCounterStride * (kPools + 1);
