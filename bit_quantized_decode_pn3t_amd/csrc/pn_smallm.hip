@@ -99,7 +99,7 @@ struct SmProb {
     int32_t tile0;     // first tile of this problem in the launch
     int32_t cb;        // blocks per activation chunk
     int32_t nchunks;
-    int32_t stride;    // LDS bytes per staged activation row (256 k + 32 for pn3t, 256 k + 48 for pn4t)
+    int32_t stride;    // LDS bytes per staged activation row (256 k + 56 for pn3t, 256 k + 48 for pn4t)
 };
 
 struct SmArgs {
@@ -110,11 +110,13 @@ struct SmArgs {
 };
 
 // LDS address of byte o of staged activation row m.  Rows are `stride` bytes
-// apart: a multiple of 256 plus 32 (pn3t) or 48 (pn4t), so that the distinct
-// reads of one operand load (up to 16 rows x 4 lane groups; pn3t reads 8 or
-// 16 bytes at 40g + ..., pn4t 16 bytes at 32g + 16s) spread over the banks
-// as evenly as an XOR swizzle of the rows would spread them, while an
-// operand's address stays a per-lane base plus a constant.
+// apart: a multiple of 256 plus 56 (pn3t) or 48 (pn4t), so that the distinct
+// reads of one operand load (up to 16 rows x 4 lane groups; pn3t reads 8
+// bytes at 40g + 8s, pn4t 16 bytes at 32g + 16s) spread over the banks, while
+// an operand's address stays a per-lane base plus a constant.  (Measured on
+// the M = 16 sweep: pn3t rows 32 bytes past a multiple of 256 2.76 ms a
+// token, 24, 40 or 56 bytes 2.54-2.55 ms, an XOR swizzle of 32-byte pieces
+// 2.61-2.67 ms with its address arithmetic.)
 template <int TYPE>
 __device__ __forceinline__ uint32_t xoff(uint32_t m, uint32_t stride, uint32_t o)
 {
@@ -194,7 +196,15 @@ __device__ __forceinline__ void stage_chunk(const SmProb &p, int b0, int nbc, ui
         for (int k = 0; k < kStageBatch; ++k) {
             const int i = i0 + k * NT + (int)threadIdx.x;
             const int m = i / per_row, q = i - m * per_row;
-            if (i < total) *(u32x4 *)(lds + xoff<TYPE>((uint32_t)m, (uint32_t)p.stride, 16u * q)) = v[k];
+            if (i < total) {
+                uint8_t *d = lds + xoff<TYPE>((uint32_t)m, (uint32_t)p.stride, 16u * q);
+                if constexpr (TYPE == 0) {  // pn3t rows are 8-byte aligned
+                    *(u32x2 *)d = (u32x2){v[k][0], v[k][1]};
+                    *(u32x2 *)(d + 8) = (u32x2){v[k][2], v[k][3]};
+                } else {
+                    *(u32x4 *)d = v[k];
+                }
+            }
         }
     }
 }
@@ -930,7 +940,7 @@ bool sm_dma_ok(int t, const void *W, int64_t K, bool mfma)
 // chunking: the fewest chunks of whole blocks whose M staged rows fit the LDS
 // budget, equal in size up to U blocks (every boundary a multiple of U), or
 // up to stages for gemm_rows (dma), whose ring takes part of the LDS.  Rows are
-// padded to 32 or 48 bytes past a multiple of 256 (xoff).
+// padded to 56 (pn3t) or 48 (pn4t) bytes past a multiple of 256 (xoff).
 pn_status sm_make(int t, const void *W, int64_t N, int64_t K, const void *X, int64_t ldx, int M, float *Y,
                   int64_t ldy, bool mfma, bool dma, SmProb &p)
 {
@@ -949,7 +959,7 @@ pn_status sm_make(int t, const void *W, int64_t N, int64_t K, const void *X, int
     for (;; ++nchunks) {
         cb = (nb + nchunks - 1) / nchunks;
         if (cb < nb) cb = (cb + unit - 1) / unit * unit;
-        stride = (cb * bytes_per_block + 255) / 256 * 256 + (t == 0 ? 32 : 48);
+        stride = (cb * bytes_per_block + 255) / 256 * 256 + (t == 0 ? 56 : 48);
         if (stride * M <= budget) break;
         if (cb <= unit) return PN_EUNSUPPORTED;
     }
