@@ -36,6 +36,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include <type_traits>
@@ -102,8 +103,12 @@ struct SmProb {
     int32_t stride;    // LDS bytes per staged activation row (256 k + 56 for pn3t, 256 k + 48 for pn4t)
 };
 
+#define PN_CONST __attribute__((address_space(4)))
+
 struct SmArgs {
-    const SmProb *table;  // device table, or null for the single problem p0
+    const PN_CONST SmProb *table;  // device table, or null for the single problem p0
+    const PN_CONST uint32_t *lut;  // plans: tile t of the launch is problem lut[t]
+    uint32_t *counters;            // gemm_rows plan launches: group counter at [0], finished workgroups at [64]; else null
     SmProb p0;
     int32_t count;
     int32_t total_tiles;
@@ -484,24 +489,19 @@ __device__ __forceinline__ void sm_tile(const SmProb &p, int row0, uint8_t *lds)
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 }
 
-__device__ __forceinline__ const SmProb *sm_problem(const SmArgs &a, int i)
-{
-    return a.table ? a.table + i : &a.p0;
-}
-
-__device__ __forceinline__ int sm_tile0(const SmArgs &a, int i)
-{
-    if (i >= a.count) return a.total_tiles;
-    return a.table ? a.table[i].tile0 : a.p0.tile0;
-}
-
-// The problem of `tile` (the tiles of a launch go through the problems in
-// order): advance i to it and load its record, wave-uniform.
+// The problem of `tile`: its index i, its record p and the first tile of
+// the next problem (next0), wave-uniform; a plan's records and tile table are
+// read with scalar loads.
 __device__ __forceinline__ void sm_next_problem(const SmArgs &args, int tile, int &i, int &next0, SmProb &p)
 {
-    if (next0 >= 0) ++i;
-    while (sm_tile0(args, i + 1) <= tile) ++i;
-    const SmProb &c = *sm_problem(args, i);
+    if (!args.table) {
+        i = 0;
+        p = args.p0;
+        next0 = args.total_tiles;
+        return;
+    }
+    i = uniform((int)args.lut[tile]);
+    const PN_CONST SmProb &c = args.table[i];
     p.W = uniform_ptr(c.W);
     p.X = uniform_ptr(c.X);
     p.Y = uniform_ptr(c.Y);
@@ -515,7 +515,7 @@ __device__ __forceinline__ void sm_next_problem(const SmArgs &args, int tile, in
     p.cb = uniform(c.cb);
     p.nchunks = uniform(c.nchunks);
     p.stride = uniform(c.stride);
-    next0 = uniform(sm_tile0(args, i + 1));
+    next0 = i + 1 < args.count ? uniform(args.table[i + 1].tile0) : args.total_tiles;
 }
 
 // Workgroups take tiles (kSmWaves x 32 rows of one problem) in a grid
@@ -615,7 +615,8 @@ constexpr int kDmStage = 16 * kDmRows * kDmChunks;                // LDS bytes p
 constexpr int kDmLast = kDmRows * kDmChunks - 64 * (kDmDma - 1);  // lanes of the last DMA instruction
 constexpr int kDmGroup = PN_SM_DMA_GROUP;                         // consecutive tiles per grid-stride step
 constexpr int kDmRing = kDmWaves * kDmStage;                      // 68 KiB
-constexpr int kDmLdsX = kSmLdsMax - kDmRing;                      // activation chunk budget
+constexpr int kDmSlots = kSmLdsMax - 256;                         // LDS: the next group's index (2 slots)
+constexpr int kDmLdsX = kDmSlots - kDmRing;                       // activation chunk budget
 static_assert(kDmPPS >= 1 && kDmPPS <= 2 && kDmThreads <= 1024 && kDmRing < kSmLdsMax, "ring shape");
 
 // Where one wave's rows of a tile are: the resource covering its valid
@@ -813,15 +814,27 @@ __device__ __forceinline__ void dm_tile(const SmProb &p, int row0, const DmSrc &
     }
 }
 
-// Workgroups take tiles (kDmWaves x 16 rows of one problem) in a grid
-// stride, as gemm_stream does; the ring sits above the activation chunk.
-// A wave's stages run on from one tile into the next without draining.
+// Workgroups take groups of kDmGroup consecutive tiles (kDmWaves x 16 rows
+// of one problem each; the activations staged for a problem serve every
+// tile of a group).  Workgroup b's first group is group b; a single call
+// then takes every gridDim-th group after it, and a plan launch takes its
+// later groups from the plan's counter (one atomic per group, issued a group
+// ahead by one lane and handed to the other waves through LDS), so that
+// workgroups that finish early take more: a plan's problems repeat with a
+// period that a grid stride can map onto the same XCDs every time (the
+// 27B-shaped layer has 104 groups, so its heavy down-projection groups
+// fell twice on XCDs 6 and 7 and once on the others in all 64 layers, and
+// those two XCDs ended the M = 8 sweep 17 % after the rest).  The last
+// workgroup to finish resets the counters for the plan's next run.  The
+// ring sits above the activation chunk, and a wave's stages run on from
+// one tile into the next without draining.
 __global__ __launch_bounds__(kDmThreads) void gemm_rows(SmArgs args)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     uint8_t *ring = lds + kDmLdsX + wave * kDmStage;
+    uint32_t *slot = (uint32_t *)(lds + kDmSlots);
     uint32_t rr[kDmDma], cc[kDmDma];
 #pragma unroll
     for (int i = 0; i < kDmDma; ++i) {
@@ -829,24 +842,74 @@ __global__ __launch_bounds__(kDmThreads) void gemm_rows(SmArgs args)
         rr[i] = q / kDmChunks;
         cc[i] = q - kDmChunks * rr[i];
     }
-    // kDmGroup consecutive tiles per step of the grid stride: the activations
-    // staged for a problem serve all of its tiles in the group
     const int groups = (args.total_tiles + kDmGroup - 1) / kDmGroup;
-    auto tile_at = [&](int k) {  // the workgroup's k-th tile, or -1
-        const int g = (int)blockIdx.x + (k / kDmGroup) * (int)gridDim.x, t = g * kDmGroup + k % kDmGroup;
+    const bool dyn = args.counters != nullptr;
+    const bool grabber = dyn && wave == 0 && lane == 0;
+    auto count_done = [&]() {
+        if (grabber) {
+            const uint32_t d = __hip_atomic_fetch_add(args.counters + 64, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (d == gridDim.x - 1) {  // every workgroup has made its last grab
+                __hip_atomic_store(args.counters, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(args.counters + 64, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    };
+    int gcur = (int)blockIdx.x;
+    if (gcur >= groups) {
+        count_done();
+        return;
+    }
+    // The grab: an atomic add issued from inline asm, its result register
+    // tied in and out, so that the compiler neither reads it at once (its own
+    // atomic waited for the result right away, draining the stage in flight)
+    // nor copies it before the atomic has written it.  It is read at the next
+    // group, after the stage waits (vmcnt(0)) of at least one tile.
+    uint32_t gr = 0;  // the grabbing lane: result of the outstanding grab
+    auto grab = [&]() {
+        asm volatile("global_atomic_add %0, %1, %2, off sc0" : "+v"(gr) : "v"(args.counters), "v"(1u) : "memory");
+    };
+    if (grabber) {
+        grab();
+        asm volatile("s_waitcnt vmcnt(0)" : "+v"(gr) :: "memory");  // nothing else is in flight yet
+    }
+    int gj = 0, gafter = 0;  // gcur's ordinal among the workgroup's groups; the group after it
+    auto next_group = [&]() {  // every wave: gafter from gcur
+        if (!dyn) {
+            gafter = gcur + (int)gridDim.x;
+            return;
+        }
+        if (grabber) {
+            asm volatile("" : "+v"(gr) :: "memory");  // read only here, after the stage waits
+            const uint32_t ga = gridDim.x + gr;
+            slot[gj & 1] = ga;
+            if ((int)ga < groups) grab();
+        }
+        // a bare barrier (__syncthreads' fence would drain the stage in
+        // flight); the slot's write has left the wave before it
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        gafter = uniform((int)slot[gj & 1]);
+    };
+    auto tile_of = [&](int g, int s) {  // tile s of group g, or -1
+        const int t = g * kDmGroup + s;
         return g < groups && t < args.total_tiles ? t : -1;
     };
-    int t = tile_at(0);
-    if (t < 0) return;
+    next_group();
+    int sub = 0;
+    int t = tile_of(gcur, 0);
     int i = 0, next0 = -1, staged = -1;
     SmProb p;
     sm_next_problem(args, t, i, next0, p);
     int row0 = ((t - p.tile0) * kDmWaves + wave) * kDmRows;
     DmSrc d = dm_src(p, row0);
     dm_issue(d, 0, ring, rr, cc, lane);
-    for (int k = 0;; ++k) {
-        // the next tile, looked up ahead so that its first stage can be issued early
-        const int tn = tile_at(k + 1);
+    for (;;) {
+        // the next tile (of this group, or the first of the next), looked up
+        // ahead so that its first stage can be issued early
+        const int ts = sub + 1 < kDmGroup ? tile_of(gcur, sub + 1) : -1;
+        const int tn = ts >= 0 ? ts : tile_of(gafter, 0);
         SmProb pn = p;
         int in = i, nn = next0, rn = 0;
         DmSrc dn = d;
@@ -871,6 +934,14 @@ __global__ __launch_bounds__(kDmThreads) void gemm_rows(SmArgs args)
         else
             dm_tile<1>(p, row0, d, dn, tn >= 0, lds, ring, rr, cc);
         if (tn < 0) break;
+        if (ts >= 0) {
+            ++sub;
+        } else {
+            gcur = gafter;
+            sub = 0;
+            ++gj;
+            next_group();
+        }
         p = pn;
         i = in;
         next0 = nn;
@@ -879,6 +950,7 @@ __global__ __launch_bounds__(kDmThreads) void gemm_rows(SmArgs args)
     }
     // no DMA or store may be outstanding when the wave ends
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    count_done();
 }
 
 // ---------------------------------------------------------------------------
@@ -981,6 +1053,16 @@ pn_status sm_make(int t, const void *W, int64_t N, int64_t K, const void *X, int
 
 int sm_lds(const SmProb &p) { return p.M * p.stride; }
 
+// A small-M plan's device memory: the problem table, the tile table (the
+// problem of each tile), then for gemm_rows the group counter ([0]) and the
+// count of finished workgroups ([64]).
+constexpr size_t kSmCounterBytes = 512;
+size_t sm_lut_offset(int count) { return (sizeof(SmProb) * (size_t)count + 15) & ~(size_t)15; }
+size_t sm_counter_offset(int count, int tiles)
+{
+    return (sm_lut_offset(count) + sizeof(uint32_t) * (size_t)tiles + 255) & ~(size_t)255;
+}
+
 pn_status sm_launch(const SmArgs &a, int lds, bool mfma, bool dma, hipStream_t s, int variant)
 {
     if (!once_per_device(kAttrSmallM, set_smallm_attr)) return PN_ELAUNCH;
@@ -1004,11 +1086,13 @@ pn_status pn::host::smallm_group_run(const pn_group *g, hipStream_t s)
 {
     SmArgs a;
     memset(&a, 0, sizeof(a));
-    a.table = (const SmProb *)g->table;
+    a.table = (const PN_CONST SmProb *)g->table;
+    a.lut = (const PN_CONST uint32_t *)((const uint8_t *)g->table + sm_lut_offset(g->count));
     a.count = g->count;
     a.total_tiles = g->total_tiles;
     const bool mfma = (g->flags & 0xf) == PN_SMALLM_MFMA;
     const bool dma = (g->flags & kSmFlagDma) != 0;
+    if (dma) a.counters = (uint32_t *)((uint8_t *)g->table + sm_counter_offset(g->count, g->total_tiles));
     return sm_launch(a, g->lds, mfma, dma, s,
                      dma ? kVarGroupSmallMRows : mfma ? kVarGroupSmallMMfma : kVarGroupSmallMValu);
 }
@@ -1052,10 +1136,18 @@ pn_status pn_group_create_smallm(const pn_gemm_desc *descs, int count, pn_group 
         const pn_gemm_desc &e = descs[i];
         st = sm_make(e.type, e.W, e.N, e.K, e.X, e.ldx, e.M, e.Y, e.ldy, math == PN_SMALLM_MFMA, dma, host[i]);
         if (st != PN_OK) break;
-        host[i].tile0 = (int32_t)tiles;
-        tiles += (e.N + rows - 1) / rows;
-        if (tiles > INT32_MAX) st = PN_EUNSUPPORTED;
         if (sm_lds(host[i]) > lds) lds = sm_lds(host[i]);
+    }
+    // The launch takes the problems' tiles in the table's order, longest rows
+    // first (stable), so that the last tiles handed out are short ones: the
+    // 27B-shaped layer's down projection (9,248-byte rows) in layer order
+    // left one workgroup on a 4.7 MB group 0.25 ms after the others.
+    if (st == PN_OK)
+        std::stable_sort(host, host + count, [](const SmProb &x, const SmProb &y) { return x.nb > y.nb; });
+    for (int i = 0; i < count && st == PN_OK; ++i) {
+        host[i].tile0 = (int32_t)tiles;
+        tiles += (host[i].N + rows - 1) / rows;
+        if (tiles > INT32_MAX) st = PN_EUNSUPPORTED;
     }
     if (st != PN_OK) {
         free(host);
@@ -1071,18 +1163,35 @@ pn_status pn_group_create_smallm(const pn_gemm_desc *descs, int count, pn_group 
         free(g);
         return PN_EUNSUPPORTED;
     }
-    if (hipMalloc(&g->table, sizeof(SmProb) * (size_t)count) != hipSuccess) {
+    // the problem table, the tile table, then (gemm_rows) the group counter
+    // and the count of finished workgroups, zero, 256 bytes apart
+    const size_t lut_off = sm_lut_offset(count), coff = sm_counter_offset(count, (int)tiles);
+    const size_t bytes = coff + (dma ? kSmCounterBytes : 0);
+    uint8_t *blob = (uint8_t *)calloc(1, bytes);
+    if (!blob) {
         free(host);
         free(g);
         return PN_ENOMEM;
     }
-    if (hipMemcpy(g->table, host, sizeof(SmProb) * (size_t)count, hipMemcpyHostToDevice) != hipSuccess) {
+    memcpy(blob, host, sizeof(SmProb) * (size_t)count);
+    uint32_t *lut = (uint32_t *)(blob + lut_off);
+    for (int i = 0; i < count; ++i) {
+        const int64_t end = i + 1 < count ? host[i + 1].tile0 : tiles;
+        for (int64_t t = host[i].tile0; t < end; ++t) lut[t] = (uint32_t)i;
+    }
+    free(host);
+    if (hipMalloc(&g->table, bytes) != hipSuccess) {
+        free(blob);
+        free(g);
+        return PN_ENOMEM;
+    }
+    if (hipMemcpy(g->table, blob, bytes, hipMemcpyHostToDevice) != hipSuccess) {
         (void)hipFree(g->table);
-        free(host);
+        free(blob);
         free(g);
         return PN_ELAUNCH;
     }
-    free(host);
+    free(blob);
     g->kind = kGroupSmallM;
     g->device = current_device();
     g->count = count;
