@@ -677,7 +677,10 @@ __device__ __forceinline__ void dm_tile(const SmProb &p, int row0, const DmSrc &
 
     int cbase = 0;                      // first block of the staged chunk
     int cnext = cb < nb ? cb : nb + 1;  // block at which the next chunk is staged
-    for (int s = 0; s < nst; ++s) {
+    // a tile has at least one stage (rows are whole periods): a do-while, so
+    // that every path through a tile passes its stage waits
+    int s = 0;
+    do {
         const int b0 = 8 * kDmPPS * s;
         const int nv = nper - kDmPPS * s < kDmPPS ? nper - kDmPPS * s : kDmPPS;  // periods in this stage
         if (b0 == cnext) {
@@ -805,7 +808,7 @@ __device__ __forceinline__ void dm_tile(const SmProb &p, int row0, const DmSrc &
             else if (nv == pp)
                 lgkm_wait<0>(xa);
         });
-    }
+    } while (++s < nst);
     // lane (jm, gm) holds D[m = 4gm + i][row jm]
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

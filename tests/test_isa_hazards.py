@@ -368,7 +368,7 @@ def test_no_cache_maintenance(tmp_path, src):
 LDS_RETURNS = ("ds_read", "ds_bpermute", "ds_permute", "ds_swizzle")
 
 
-def _lds_returns(op):
+def _lds_returns(op, line=""):
     return op.startswith(LDS_RETURNS) or (op.startswith("ds_") and "_rtn" in op)
 
 
@@ -377,6 +377,31 @@ def find_lds_use_before_wait(asm, cap=64):
     filling, on some path (forward dataflow over the control-flow graph; the
     state maps each read to the fewest younger LDS reads issued after it on
     any path reaching the point)."""
+    return _use_before_wait(asm, _lds_returns, _lds_returns, "lgkmcnt", cap)
+
+
+def _vmem_returns(op, line):
+    """Vector memory instructions that write a VGPR result: loads into
+    registers and atomics that return (sc0), not stores or LDS DMA."""
+    if op.startswith(("global_load", "buffer_load", "flat_load", "scratch_load")):
+        return not line.rstrip().endswith(" lds") and " lds" not in line.split(";")[0].split(",")[-1]
+    if op.startswith(("global_atomic", "buffer_atomic", "flat_atomic")):
+        return " sc0" in line or " glc" in line
+    return False
+
+
+def _vmem_counts(op, line):
+    return op.startswith(("global_", "buffer_", "flat_", "scratch_"))
+
+
+def find_vmem_use_before_wait(asm, cap=64):
+    """The same for vector memory results (a hand-issued atomic's result must
+    not be touched before a vmcnt wait retires it); every vector memory
+    instruction counts as younger, as the compiler counts them."""
+    return _use_before_wait(asm, _vmem_returns, _vmem_counts, "vmcnt", cap)
+
+
+def _use_before_wait(asm, returns, counts, counter, cap):
     blocks, labels, succ = _blocks(asm)
     entry = [None] * len(blocks)
     entry[0] = {}
@@ -393,19 +418,28 @@ def find_lds_use_before_wait(asm, cap=64):
         for ii, line in enumerate(blocks[bi]):
             op, args = _split(line)
             if op == "s_waitcnt":
-                m = re.search(r"lgkmcnt\((\d+)\)", line)
+                m = re.search(counter + r"\((\d+)\)", line)
                 if m:
                     n = int(m.group(1))
                     st = {k: v for k, v in st.items() if v[0] < n}
                 continue
             regs = set()
-            for t in args:
-                regs |= _regs2(t.split()[0]) if t else set()
+            for j, t in enumerate(args):
+                rs = _regs2(t.split()[0]) if t else set()
+                # the compiler does 32-bit multiply-adds with v_mad_u64_u32
+                # and leaves the addend's high half undefined: not a use
+                if j == 4 and op.startswith("v_mad_u64_u32") and len(rs) == 2:
+                    rs = {min(rs)}
+                regs |= rs
+            # a younger read of the same kind into the same registers lands
+            # after the older one (they return in order)
+            ordered = returns(op, line)
             for key, (newer, dst) in st.items():
-                if dst & regs and record:
+                if dst & regs and record and not ordered:
                     found.add("%s touches the registers of %s before its wait" % (line, key[2]))
-            if _lds_returns(op) and args:
+            if counts(op, line):
                 st = {k: (min(v[0] + 1, cap), v[1]) for k, v in st.items()}
+            if returns(op, line) and args:
                 st[(bi, ii, line)] = (0, _regs2(args[0].split()[0]))
         return st
 
@@ -496,3 +530,59 @@ def test_small_m_kernels_wait_for_their_lds_reads(tmp_path):
     asm = _compile(tmp_path, os.path.join(os.path.dirname(SRC), "pn_smallm.hip"), "pn_smallm.hip")
     assert len(re.findall(r"^\s*ds_read2_b64", asm, re.M)) >= 16  # the read-ahead operands are there
     assert find_lds_use_before_wait(asm) == []
+
+
+def test_vmem_wait_checker_flags_planted_uses():
+    planted = """
+_kernel:
+    global_atomic_add v1, v[4:5], v3, off sc0
+    buffer_load_dwordx4 v10, s[8:11], 0 offen lds
+    v_add_u32_e32 v7, v1, v2
+    s_waitcnt vmcnt(1)
+    v_add_u32_e32 v8, v1, v2
+    global_load_dword v20, v[4:5], off
+    global_load_dword v22, v[4:5], off offset:4
+    s_waitcnt vmcnt(1)
+    v_mov_b32_e32 v21, v20
+    global_store_dword v[4:5], v22, off
+    global_load_dword v20, v[4:5], off offset:8
+    s_endpgm
+"""
+    got = find_vmem_use_before_wait(planted)
+    # v7 <- v1 before any wait; the store of v22 with its load possibly still
+    # outstanding after vmcnt(1); not v8 <- v1 (the DMA load is younger than
+    # the atomic), not v21 <- v20 (one younger load), not the second load
+    # into v20 (loads return in order)
+    assert len(got) == 2, got
+    assert any(g.startswith("v_add_u32_e32 v7, v1") for g in got), got
+    assert any(g.startswith("global_store_dword v[4:5], v22") for g in got), got
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None, reason="no hipcc")
+def test_row_tile_grabs_are_waited_for(tmp_path):
+    """The row-tile kernel's grabs are atomics issued from inline asm whose
+    result is read a step later: no instruction may touch the result register
+    before a vmcnt wait has retired the atomic, on any path."""
+    asm = _compile(tmp_path, SRC, "rows")
+    assert len(re.findall(r"^\s*global_atomic_add v\d+, v\[\d+:\d+\], v\d+, off sc0", asm, re.M)) >= 1
+    assert find_vmem_use_before_wait(asm) == []
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None, reason="no hipcc")
+def test_small_m_grabs_are_not_touched_early(tmp_path):
+    """The small-M DMA kernel's group grab is read a group later, after at
+    least one tile, whose every stage starts with an unconditional vmcnt(0)
+    (the stage loop is a do-while).  The compiler wraps the tile in
+    exec-masked regions, so the control-flow check above sees paths on which
+    those regions are empty and the waits skipped, which no wave takes (every
+    lane enters the tile); here the straight-line check asks that nothing
+    touches the result register between the atomic and the first branch or
+    wait, and the source keeps the read behind an asm statement tied to the
+    register."""
+    src = os.path.join(os.path.dirname(SRC), "pn_smallm.hip")
+    asm = _compile(tmp_path, src, "smallm")
+    assert len(re.findall(r"^\s*global_atomic_add v\d+, v\[\d+:\d+\], v\d+, off sc0", asm, re.M)) >= 2
+    assert find_hazards(asm) == []
+    text = open(src).read()
+    assert 'asm volatile("" : "+v"(gr) :: "memory");  // read only here, after the stage waits' in text
+    assert "} while (++s < nst);" in text
