@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpn.so")
 # Every symbol include/pn.h declares.
 EXPORTS = ("pn_weights_per_block", "pn_row_bytes", "pn_gemv", "pn_gemv2",
            "pn_gemm_smallm", "pn_set_smallm_math", "pn_get_smallm_math", "pn_set_gemv_kernel",
-           "pn_get_gemv_kernel", "pn_dequantize", "pn_rotate", "pn_gemm_prefill",
+           "pn_get_gemv_kernel", "pn_dequantize", "pn_rotate", "pn_gemm_prefill", "pn_gemm_prefill_group",
            "pn_group_create", "pn_group_create_smallm", "pn_group_run", "pn_group_destroy", "pn_gemv_batch",
            "pn_read_probe_scratch_bytes", "pn_read_probe", "pn_status_str", "pn_last_variant",
            "pn_variant_name")
@@ -88,6 +88,8 @@ def lib():
     L.pn_get_smallm_math.restype = i32
     L.pn_group_create_smallm.argtypes = [ctypes.POINTER(pn_gemm_desc), i32, ctypes.POINTER(vp)]
     L.pn_group_create_smallm.restype = i32
+    L.pn_gemm_prefill_group.argtypes = [ctypes.POINTER(pn_gemm_desc), i32, vp]
+    L.pn_gemm_prefill_group.restype = i32
     L.pn_dequantize.argtypes = [i32, vp, i64, i64, vp, vp]
     L.pn_dequantize.restype = i32
     L.pn_rotate.argtypes = [vp, i64, i32, i64, vp, i64, vp]
@@ -215,6 +217,20 @@ def pn_gemm_prefill(pn_type, W, N, K, X, ldx, M, Y, ldy, stream=None, check=True
     st = lib().pn_gemm_prefill(_t(pn_type), _ptr(W), N, K, _ptr(X), ldx, M, _ptr(Y), ldy, _stream(stream))
     if check:
         _check(st, "pn_gemm_prefill")
+    return st
+
+
+PREFILL_GROUP_MAX = 8  # PN_PREFILL_GROUP_MAX
+
+
+def pn_gemm_prefill_group(problems, stream=None, check=True):
+    """Run (pn_type, W, N, K, X, ldx, M, Y, ldy) prefill problems as one launch."""
+    arr = (pn_gemm_desc * max(len(problems), 1))()
+    for i, (t, W, N, K, X, ldx, M, Y, ldy) in enumerate(problems):
+        arr[i] = pn_gemm_desc(_ptr(W), _ptr(X), _ptr(Y), N, K, ldx, ldy, _t(t), M)
+    st = lib().pn_gemm_prefill_group(arr, len(problems), _stream(stream))
+    if check:
+        _check(st, "pn_gemm_prefill_group")
     return st
 
 

@@ -30,6 +30,7 @@ enum Variant {
     kVarGroupSmallMRows = 14,
     kVarBatchRows = 15,
     kVarBatchStream = 16,
+    kVarPrefillGroup = 17,
 };
 
 extern thread_local int g_last_variant;

@@ -967,6 +967,7 @@ const char *pn_variant_name(int v)
     case kVarGroupRows: return "gemv_rows_group";
     case kVarRotate: return "hadamard_rotate";
     case kVarPrefill: return "gemm_prefill";
+    case kVarPrefillGroup: return "gemm_prefill_group";
     case kVarDequant: return "dequant";
     case kVarGroupStream: return "gemv_stream_group";
     case kVarBatchRows: return "gemv_rows_batch";

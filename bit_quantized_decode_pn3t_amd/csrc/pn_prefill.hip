@@ -1,5 +1,6 @@
 // pn_prefill.hip - PN GEMM for prefill (any number of activation rows), for
-// AMD Instinct MI355X (gfx950), and its C ABI: pn_gemm_prefill.
+// AMD Instinct MI355X (gfx950), and its C ABI: pn_gemm_prefill and
+// pn_gemm_prefill_group.
 //
 // Y[m, r] = sum_k w[r, k] X[m, k] for m < M, w = d * (n - z) ("Exact decode
 // in fp32").  The pages' engine handles prefill by dequantizing PN weights
@@ -24,7 +25,10 @@
 // two stages while the other is computed, and each wave decodes its 32
 // weight rows straight into B operands.
 //
-// Work.  One workgroup per CU, persistent.  The launch's tiles would leave
+// Work.  One launch takes one product or several (up to 8, of either type,
+// numbered one after another: a decoder layer's q, k and v, or gate and
+// up, whose tiles alone leave part of the device idle).  One workgroup per
+// CU, persistent.  The launch's tiles would leave
 // the last round of workgroups part empty (272 gate tiles on 256 CUs take
 // two rounds of the same length), so the tiles of whole rounds are dealt
 // whole (tile t to workgroup t mod G, plain stores) and each of the R
@@ -102,16 +106,60 @@ struct Pf {
     static_assert(kPfM * XSL % 64 == 0 && kPfN * kPairDw % 64 == 0, "whole DMA instructions");
 };
 
-struct PfArgs {
+constexpr int kPfLds = Pf<0>::LDS > Pf<1>::LDS ? Pf<0>::LDS : Pf<1>::LDS;
+constexpr int kPfGroupMax = 8;  // products per launch (PN_PREFILL_GROUP_MAX)
+
+// One product of a launch.
+struct PfProb {
     const uint8_t *W;  // packed rows
     const uint16_t *X;
     float *Y;
     int64_t ldx, ldy;
     int32_t N, M, S, pairs;  // S: row bytes; pairs: block pairs per row
-    int32_t tn, tiles;       // tiles along N, tiles (tile t: N tile t % tn, M tile t / tn)
-    int32_t t1;              // tiles [0, t1) dealt whole, a whole number of rounds
-    int32_t ways;            // workgroups sharing each of tiles [t1, tiles) (0: none shared)
+    int32_t tn;              // tiles along N (the product's tile u: N tile u % tn, M tile u / tn)
+    int32_t tile0;           // the product's first tile in the launch
+    int32_t type;
+    int32_t pad;
 };
+
+// The launch's products (by value: no device table, nothing allocated) and
+// how its tiles are dealt.
+struct PfArgs {
+    PfProb prob[kPfGroupMax];
+    int32_t count;
+    int32_t tiles;  // all products' tiles
+    int32_t t1;     // tiles [0, t1) dealt whole, a whole number of rounds
+    int32_t ways;   // workgroups sharing each of tiles [t1, tiles) (0: none shared)
+};
+
+// The product that launch tile t belongs to, read from the launch's
+// argument segment with scalar loads (a dynamic index into the by-value
+// argument would make the compiler copy the whole array to scratch).
+#define PF_KARG __attribute__((address_space(4)))
+__device__ __forceinline__ PfProb pf_problem(int t)
+{
+    const PF_KARG PfArgs *k = (const PF_KARG PfArgs *)__builtin_amdgcn_kernarg_segment_ptr();
+    int i = 0;
+#pragma unroll
+    for (int j = 1; j < kPfGroupMax; ++j)
+        if (j < k->count && t >= k->prob[j].tile0) i = j;
+    const PF_KARG PfProb &q = k->prob[i];
+    PfProb p;
+    p.W = q.W;
+    p.X = q.X;
+    p.Y = q.Y;
+    p.ldx = q.ldx;
+    p.ldy = q.ldy;
+    p.N = q.N;
+    p.M = q.M;
+    p.S = q.S;
+    p.pairs = q.pairs;
+    p.tn = q.tn;
+    p.tile0 = q.tile0;
+    p.type = q.type;
+    p.pad = 0;
+    return p;
+}
 
 __device__ __forceinline__ half8_t cat4(half2_t a, half2_t b, half2_t c, half2_t d)
 {
@@ -183,121 +231,137 @@ __device__ __forceinline__ void stage_pair(uint8_t *st, const __amdgpu_buffer_rs
     }
 }
 
+// Block pairs [p0, p1) of tile u of product a (N tile u % tn, M tile u / tn),
+// stored (add = false) or added into Y.  Every wave of the workgroup calls
+// this with the same arguments.
 template <int TYPE>
-__global__ __launch_bounds__(kPfThreads) void gemm_prefill(PfArgs a)
+__device__ __forceinline__ void pf_piece(const PfProb &a, int u, int p0, int p1, bool add, uint8_t *lds, int wave,
+                                         int lane)
 {
     using C = Pf<TYPE>;
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int lane = threadIdx.x & 63;
-    const int wave = (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave % kWM, wn = wave / kWM;
     const int h = lane >> 5, c = lane & 31;
     const uint32_t xrow = (uint32_t)a.ldx * 2u, wrow = (uint32_t)a.S;
     uint32_t xo[C::XPER], wo[C::WPER];
     pf_offsets<TYPE>(xo, wo, xrow, wrow, wave, lane);
 
-    // Block pairs [p0, p1) of tile t, stored (add = false) or added into Y.
-    auto piece = [&](int t, int p0, int p1, bool add) {
-        const int n0 = (t % a.tn) * kPfN, m0 = (t / a.tn) * kPfM;
-        const int xrows = a.M - m0 < kPfM ? a.M - m0 : kPfM;
-        const int wrows = a.N - n0 < kPfN ? a.N - n0 : kPfN;
-        const __amdgpu_buffer_rsrc_t xr = rsrc(a.X + (int64_t)m0 * a.ldx, (uint32_t)xrows * xrow);
-        const __amdgpu_buffer_rsrc_t wr = rsrc(a.W + (int64_t)n0 * a.S, (uint32_t)wrows * wrow);
+    const int n0 = (u % a.tn) * kPfN, m0 = (u / a.tn) * kPfM;
+    const int xrows = a.M - m0 < kPfM ? a.M - m0 : kPfM;
+    const int wrows = a.N - n0 < kPfN ? a.N - n0 : kPfN;
+    const __amdgpu_buffer_rsrc_t xr = rsrc(a.X + (int64_t)m0 * a.ldx, (uint32_t)xrows * xrow);
+    const __amdgpu_buffer_rsrc_t wr = rsrc(a.W + (int64_t)n0 * a.S, (uint32_t)wrows * wrow);
 
-        float16_t acc[kMT][kNT];
+    float16_t acc[kMT][kNT];
 #pragma unroll
-        for (int i = 0; i < kMT; ++i)
+    for (int i = 0; i < kMT; ++i)
 #pragma unroll
-            for (int j = 0; j < kNT; ++j) acc[i][j] = (float16_t){};
+        for (int j = 0; j < kNT; ++j) acc[i][j] = (float16_t){};
 
-        // every wave is done with the stages of the workgroup's last piece
+    // every wave is done with the stages of the workgroup's last piece
+    __syncthreads();
+    stage_pair<TYPE>(lds, xr, wr, xo, wo, p0, wave);
+    for (int p = p0; p < p1; ++p) {
+        // this wave's loads of pair p have landed; after the barrier, every
+        // wave's have, and every wave is done with pair p - 1's stage
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
         __syncthreads();
-        stage_pair<TYPE>(lds, xr, wr, xo, wo, p0, wave);
-        for (int p = p0; p < p1; ++p) {
-            // this wave's loads of pair p have landed; after the barrier, every
-            // wave's have, and every wave is done with pair p - 1's stage
-            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-            __syncthreads();
-            uint8_t *st = lds + ((p - p0) & 1) * C::STAGE;
-            if (p + 1 < p1) stage_pair<TYPE>(lds + ((p - p0 + 1) & 1) * C::STAGE, xr, wr, xo, wo, p + 1, wave);
-            const uint16_t *xs = (const uint16_t *)st;
-            const uint32_t *ws = (const uint32_t *)(st + C::XBYTES);
+        uint8_t *st = lds + ((p - p0) & 1) * C::STAGE;
+        if (p + 1 < p1) stage_pair<TYPE>(lds + ((p - p0 + 1) & 1) * C::STAGE, xr, wr, xo, wo, p + 1, wave);
+        const uint16_t *xs = (const uint16_t *)st;
+        const uint32_t *ws = (const uint32_t *)(st + C::XBYTES);
 
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                // decode: the lane's four words of block b, for its row of each N tile
-                half2_t u[kNT][4][TYPE == 0 ? 5 : 4];
-                float d[kNT];
-#pragma unroll
-                for (int nt = 0; nt < kNT; ++nt) {
-                    const uint32_t *pw = ws + (wn * 32 * kNT + nt * 32 + c) * kPairDw;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        Unpack<TYPE>::run(pair_word(pw, b, TYPE == 0 ? 4 * h + j : h + 2 * j), u[nt][j]);
-                    d[nt] = pair_scale(pw, b);
-                }
-                float16_t P[kMT][kNT];  // the block's fresh accumulators
-#pragma unroll
-                for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-                    for (int nt = 0; nt < kNT; ++nt) P[mt][nt] = (float16_t){};
-#pragma unroll
-                for (int s = 0; s < C::STEPS; ++s) {
-                    half8_t B[kNT];
-#pragma unroll
-                    for (int nt = 0; nt < kNT; ++nt) {
-                        if constexpr (TYPE == 0)  // the lane's code pairs 4s .. 4s+3 (pair i: word i / 5, pair i % 5)
-                            B[nt] = cat4(u[nt][(4 * s) / 5][(4 * s) % 5], u[nt][(4 * s + 1) / 5][(4 * s + 1) % 5],
-                                         u[nt][(4 * s + 2) / 5][(4 * s + 2) % 5], u[nt][(4 * s + 3) / 5][(4 * s + 3) % 5]);
-                        else
-                            B[nt] = cat4(u[nt][s][0], u[nt][s][1], u[nt][s][2], u[nt][s][3]);
-                    }
-#pragma unroll
-                    for (int mt = 0; mt < kMT; ++mt) {
-                        const uint16_t *px = xs + (wm * 32 * kMT + mt * 32 + c) * (8 * C::XSL);
-                        const int k = TYPE == 0 ? 80 * b + 40 * h + 8 * s : 64 * b + 16 * s + 8 * h;
-                        const half8_t A = __builtin_bit_cast(half8_t, *(const u32x4 *)(px + k));
-#pragma unroll
-                        for (int nt = 0; nt < kNT; ++nt)
-                            P[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B[nt], P[mt][nt], 0, 0, 0);
-                    }
-                }
-#pragma unroll
-                for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-                    for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) acc[mt][nt][v] = __builtin_fmaf(d[nt], P[mt][nt][v], acc[mt][nt][v]);
-            }
-        }
-
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt)
+        for (int b = 0; b < 2; ++b) {
+            // decode: the lane's four words of block b, for its row of each N tile
+            half2_t u[kNT][4][TYPE == 0 ? 5 : 4];
+            float d[kNT];
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) {
-                const int n = n0 + wn * 32 * kNT + nt * 32 + c;
+                const uint32_t *pw = ws + (wn * 32 * kNT + nt * 32 + c) * kPairDw;
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int m = m0 + wm * 32 * kMT + mt * 32 + 8 * (v / 4) + 4 * h + (v % 4);
-                    if (m < a.M && n < a.N) {
-                        float *y = a.Y + (int64_t)m * a.ldy + n;
-                        if (add)
-                            __hip_atomic_fetch_add(y, acc[mt][nt][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        else
-                            *y = acc[mt][nt][v];
-                    }
+                for (int j = 0; j < 4; ++j)
+                    Unpack<TYPE>::run(pair_word(pw, b, TYPE == 0 ? 4 * h + j : h + 2 * j), u[nt][j]);
+                d[nt] = pair_scale(pw, b);
+            }
+            float16_t P[kMT][kNT];  // the block's fresh accumulators
+#pragma unroll
+            for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < kNT; ++nt) P[mt][nt] = (float16_t){};
+#pragma unroll
+            for (int s = 0; s < C::STEPS; ++s) {
+                half8_t B[kNT];
+#pragma unroll
+                for (int nt = 0; nt < kNT; ++nt) {
+                    if constexpr (TYPE == 0)  // the lane's code pairs 4s .. 4s+3 (pair i: word i / 5, pair i % 5)
+                        B[nt] = cat4(u[nt][(4 * s) / 5][(4 * s) % 5], u[nt][(4 * s + 1) / 5][(4 * s + 1) % 5],
+                                     u[nt][(4 * s + 2) / 5][(4 * s + 2) % 5], u[nt][(4 * s + 3) / 5][(4 * s + 3) % 5]);
+                    else
+                        B[nt] = cat4(u[nt][s][0], u[nt][s][1], u[nt][s][2], u[nt][s][3]);
+                }
+#pragma unroll
+                for (int mt = 0; mt < kMT; ++mt) {
+                    const uint16_t *px = xs + (wm * 32 * kMT + mt * 32 + c) * (8 * C::XSL);
+                    const int k = TYPE == 0 ? 80 * b + 40 * h + 8 * s : 64 * b + 16 * s + 8 * h;
+                    const half8_t A = __builtin_bit_cast(half8_t, *(const u32x4 *)(px + k));
+#pragma unroll
+                    for (int nt = 0; nt < kNT; ++nt)
+                        P[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B[nt], P[mt][nt], 0, 0, 0);
                 }
             }
-    };
+#pragma unroll
+            for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[mt][nt][v] = __builtin_fmaf(d[nt], P[mt][nt][v], acc[mt][nt][v]);
+        }
+    }
 
-    // whole tiles, one round after another
-    for (int t = blockIdx.x; t < a.t1; t += gridDim.x) piece(t, 0, a.pairs, false);
-    // then the other R tiles, workgroup w taking slice w / R of tile
-    // t1 + w % R: pairs [pairs j / ways, pairs (j + 1) / ways)
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+            const int n = n0 + wn * 32 * kNT + nt * 32 + c;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int m = m0 + wm * 32 * kMT + mt * 32 + 8 * (v / 4) + 4 * h + (v % 4);
+                if (m < a.M && n < a.N) {
+                    float *y = a.Y + (int64_t)m * a.ldy + n;
+                    if (add)
+                        __hip_atomic_fetch_add(y, acc[mt][nt][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    else
+                        *y = acc[mt][nt][v];
+                }
+            }
+        }
+}
+
+// Workgroups take the launch's tiles: those of whole rounds one after
+// another (tile t to workgroup t mod G), then the R others, workgroup w
+// taking slice j = w / R of tile t1 + w % R: its product's block pairs
+// [pairs j / ways, pairs (j + 1) / ways).
+__global__ __launch_bounds__(kPfThreads) void gemm_prefill(PfArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int lane = threadIdx.x & 63;
+    const int wave = (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int R = a.tiles - a.t1;
-    if (a.ways > 0 && (int)blockIdx.x < R * a.ways) {
-        const int j = (int)blockIdx.x / R;
-        piece(a.t1 + (int)blockIdx.x % R, a.pairs * j / a.ways, a.pairs * (j + 1) / a.ways, true);
+    const bool shares = a.ways > 0 && (int)blockIdx.x < R * a.ways;
+    // one call site, so that each type's piece is inlined once
+    for (int t = blockIdx.x;; t += gridDim.x) {
+        const bool whole = t < a.t1;
+        if (!whole && !shares) break;
+        // past the whole tiles: this workgroup's slice of a shared tile, once
+        const int tt = whole ? t : a.t1 + (int)blockIdx.x % R;
+        const int j = whole ? 0 : (int)blockIdx.x / R, ways = whole ? 0 : a.ways;
+        const PfProb p = pf_problem(tt);
+        const int p0 = ways > 0 ? p.pairs * j / ways : 0, p1 = ways > 0 ? p.pairs * (j + 1) / ways : p.pairs;
+        if (p.type == 0)
+            pf_piece<0>(p, tt - p.tile0, p0, p1, !whole, lds, wave, lane);
+        else
+            pf_piece<1>(p, tt - p.tile0, p0, p1, !whole, lds, wave, lane);
+        if (!whole) break;
     }
 }
 
@@ -308,26 +372,29 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill(PfArgs a)
 __global__ __launch_bounds__(256) void zero_tiles(PfArgs a)
 {
     const int t = a.t1 + (int)blockIdx.y;
-    const int col = (t % a.tn) * kPfN + (int)threadIdx.x;
+    const PfProb p = pf_problem(t);
+    const int u = t - p.tile0;
+    const int col = (u % p.tn) * kPfN + (int)threadIdx.x;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int m = (t / a.tn) * kPfM + 4 * (int)blockIdx.x + i;
-        if (m < a.M && col < a.N) a.Y[(int64_t)m * a.ldy + col] = 0.0f;
+        const int m = (u / p.tn) * kPfM + 4 * (int)blockIdx.x + i;
+        if (m < p.M && col < p.N) p.Y[(int64_t)m * p.ldy + col] = 0.0f;
     }
 }
 
 bool set_prefill_attr()
 {
-    return hipFuncSetAttribute((const void *)gemm_prefill<0>, hipFuncAttributeMaxDynamicSharedMemorySize, Pf<0>::LDS) ==
-               hipSuccess &&
-           hipFuncSetAttribute((const void *)gemm_prefill<1>, hipFuncAttributeMaxDynamicSharedMemorySize, Pf<1>::LDS) ==
-               hipSuccess;
+    return hipFuncSetAttribute((const void *)gemm_prefill, hipFuncAttributeMaxDynamicSharedMemorySize, kPfLds) ==
+           hipSuccess;
 }
 
 }  // namespace
 
-pn_status pn_gemm_prefill(pn_type t, const void *W, int64_t N, int64_t K, const uint16_t *X, int64_t ldx, int64_t M,
-                          float *Y, int64_t ldy, void *stream)
+namespace {
+
+// Validate one product (the checks of pn_gemm_prefill) and fill its record.
+pn_status pf_make(pn_type t, const void *W, int64_t N, int64_t K, const void *X, int64_t ldx, int64_t M, float *Y,
+                  int64_t ldy, PfProb &p)
 {
     pn_status st = check_matrix(t, W, N, K);
     if (st) return st;
@@ -340,33 +407,49 @@ pn_status pn_gemm_prefill(pn_type t, const void *W, int64_t N, int64_t K, const 
     if ((uint64_t)kPfM * (uint64_t)ldx * 2u >= 0x80000000ull) return PN_EUNSUPPORTED;  // 32-bit tile offsets
     if (N * M > ((int64_t)1 << 40)) return PN_EUNSUPPORTED;
     if ((uint64_t)kPfN * (uint64_t)nb * 34u >= 0x80000000ull) return PN_EUNSUPPORTED;  // 32-bit row offsets
+    const int64_t tn = (N + kPfN - 1) / kPfN;
+    if (tn * ((M + kPfM - 1) / kPfM) > INT32_MAX) return PN_EUNSUPPORTED;
+    memset(&p, 0, sizeof(p));
+    p.W = (const uint8_t *)W;
+    p.X = (const uint16_t *)X;
+    p.Y = Y;
+    p.ldx = ldx;
+    p.ldy = ldy;
+    p.N = (int32_t)N;
+    p.M = (int32_t)M;
+    p.S = (int32_t)(nb * 34);
+    p.pairs = (int32_t)(nb / 2);
+    p.tn = (int32_t)tn;
+    p.type = t;
+    return PN_OK;
+}
+
+int64_t pf_tiles(const PfProb &p) { return (int64_t)p.tn * ((p.M + kPfM - 1) / kPfM); }
+
+// Number the products' tiles one after another, deal them and launch.  One
+// workgroup per CU (the two LDS stages take 102-118 KiB): the tiles of whole
+// rounds are dealt whole, and the R others are each shared by `ways`
+// workgroups, as many as fit one round, at most 8 and with at least 4 block
+// pairs of every product each: the atomic adds of a shared tile cost about
+// as much as computing a few of its pairs (on 256 CUs, 16 gate tiles shared
+// 16 ways took 136 us, shared 8 ways less).
+pn_status pf_launch(PfArgs &a, hipStream_t s, int variant)
+{
     if (!once_per_device(kAttrPrefill, set_prefill_attr)) return PN_ELAUNCH;
-    PfArgs a;
-    a.W = (const uint8_t *)W;
-    a.X = X;
-    a.Y = Y;
-    a.ldx = ldx;
-    a.ldy = ldy;
-    a.N = (int32_t)N;
-    a.M = (int32_t)M;
-    a.S = (int32_t)(nb * 34);
-    a.pairs = (int32_t)(nb / 2);
-    // One workgroup per CU (the two LDS stages take 102-118 KiB): the tiles
-    // of whole rounds are dealt whole, and the R others are each shared by
-    // `ways` workgroups, as many as fit one round, at most 8 and with at
-    // least 4 block pairs each: the atomic adds of a shared tile cost about
-    // as much as computing a few of its pairs (on 256 CUs, 16 gate tiles
-    // shared 16 ways took 136 us, shared 8 ways less).
+    int64_t tiles = 0, min_pairs = INT32_MAX;
+    for (int i = 0; i < a.count; ++i) {
+        a.prob[i].tile0 = (int32_t)tiles;
+        tiles += pf_tiles(a.prob[i]);
+        if (tiles > INT32_MAX) return PN_EUNSUPPORTED;
+        if (a.prob[i].pairs < min_pairs) min_pairs = a.prob[i].pairs;
+    }
     const int64_t G = device_cus();
-    const int64_t tn = (N + kPfN - 1) / kPfN, tiles = tn * ((M + kPfM - 1) / kPfM);
-    if (tiles > INT32_MAX) return PN_EUNSUPPORTED;
-    a.tn = (int32_t)tn;
     a.tiles = (int32_t)tiles;
     a.t1 = (int32_t)(tiles / G * G);
     const int64_t R = tiles - a.t1;
     int64_t ways = R > 0 ? G / R : 1;
     if (ways > kPfMaxWays) ways = kPfMaxWays;
-    if (ways > a.pairs / 4) ways = a.pairs / 4;
+    if (ways > min_pairs / 4) ways = min_pairs / 4;
     if (ways < 2) {  // no tile is shared: the rest are dealt whole too
         a.t1 = (int32_t)tiles;
         ways = 0;
@@ -374,16 +457,39 @@ pn_status pn_gemm_prefill(pn_type t, const void *W, int64_t N, int64_t K, const 
     a.ways = (int32_t)ways;
     const int64_t g2 = R * ways;
     const int64_t grid = a.t1 > 0 ? (G < tiles ? G : tiles) : g2;
-    const hipStream_t s = (hipStream_t)stream;
     if (g2 > 0) {
         hipLaunchKernelGGL(zero_tiles, dim3(kPfM / 4, (unsigned)(tiles - a.t1)), dim3(kPfN), 0, s, a);
         if (hipGetLastError() != hipSuccess) return PN_ELAUNCH;
     }
-    if (t == PN_PN3T)
-        hipLaunchKernelGGL(gemm_prefill<0>, dim3((unsigned)grid), dim3(kPfThreads), Pf<0>::LDS, s, a);
-    else
-        hipLaunchKernelGGL(gemm_prefill<1>, dim3((unsigned)grid), dim3(kPfThreads), Pf<1>::LDS, s, a);
+    hipLaunchKernelGGL(gemm_prefill, dim3((unsigned)grid), dim3(kPfThreads), kPfLds, s, a);
     if (hipGetLastError() != hipSuccess) return PN_ELAUNCH;
-    g_last_variant = kVarPrefill;
+    g_last_variant = variant;
     return PN_OK;
+}
+
+}  // namespace
+
+pn_status pn_gemm_prefill(pn_type t, const void *W, int64_t N, int64_t K, const uint16_t *X, int64_t ldx, int64_t M,
+                          float *Y, int64_t ldy, void *stream)
+{
+    PfArgs a;
+    memset(&a, 0, sizeof(a));
+    const pn_status st = pf_make(t, W, N, K, X, ldx, M, Y, ldy, a.prob[0]);
+    if (st) return st;
+    a.count = 1;
+    return pf_launch(a, (hipStream_t)stream, kVarPrefill);
+}
+
+pn_status pn_gemm_prefill_group(const pn_gemm_desc *descs, int count, void *stream)
+{
+    if (!descs || count < 1 || count > kPfGroupMax) return PN_EINVAL;
+    PfArgs a;
+    memset(&a, 0, sizeof(a));
+    for (int i = 0; i < count; ++i) {
+        const pn_gemm_desc &e = descs[i];
+        const pn_status st = pf_make((pn_type)e.type, e.W, e.N, e.K, e.X, e.ldx, e.M, e.Y, e.ldy, a.prob[i]);
+        if (st) return st;
+    }
+    a.count = count;
+    return pf_launch(a, (hipStream_t)stream, kVarPrefillGroup);
 }

@@ -235,10 +235,22 @@ typedef struct pn_gemm_desc {
     int64_t ldx;     /* elements, >= K, even                    */
     int64_t ldy;     /* elements, >= N                          */
     int32_t type;    /* pn_type                                 */
-    int32_t M;       /* 1..16                                   */
+    int32_t M;       /* 1..16 (pn_gemm_prefill_group: >= 1)     */
 } pn_gemm_desc;
 
 pn_status pn_group_create_smallm(const pn_gemm_desc *descs, int count, pn_group **out);
+
+/* Several prefill products as one launch: the projections of a decoder layer
+ * that can run together because their inputs are ready together (q, k and v;
+ * gate and up), so that their tiles fill the device as one launch instead of
+ * three or two that each leave part of it idle.  Each entry is one
+ * pn_gemm_prefill problem (arguments, checks and results as there; M may
+ * differ between entries); the entries may mix types and shapes.  At most
+ * PN_PREFILL_GROUP_MAX entries, else PN_EINVAL; the first entry that fails a
+ * check gives the status and nothing is enqueued.  Allocates nothing (the
+ * entries travel in the launch's arguments); enqueued on `stream`. */
+#define PN_PREFILL_GROUP_MAX 8
+pn_status pn_gemm_prefill_group(const pn_gemm_desc *descs, int count, void *stream);
 
 /* Enqueue all problems of a plan (either kind) as one launch on `stream`
  * (plus the rotation launch ahead of it for PN_DESC_ROTATE entries).  Runs

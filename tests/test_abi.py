@@ -48,15 +48,15 @@ def test_host_helpers():
 def test_variant_names():
     """Every kernel the library can report has its own name; unknown ids are
     reported as such rather than as a kernel."""
-    names = [B.pn_variant_name(v) for v in range(17)]
+    names = [B.pn_variant_name(v) for v in range(18)]
     assert names[0] == "none"
     assert len(set(names)) == len(names), names
     for expect in ("gemv_rows", "gemv_rows_group", "gemv_stream", "gemv_stream_group", "gemv_generic",
                    "gemm_stream_mfma", "gemm_stream_valu", "gemm_stream_mfma_group", "gemm_stream_valu_group",
                    "gemm_rows_mfma", "gemm_rows_mfma_group", "gemm_prefill", "hadamard_rotate", "dequant",
-                   "gemv_rows_batch", "gemv_stream_batch"):
+                   "gemv_rows_batch", "gemv_stream_batch", "gemm_prefill_group"):
         assert expect in names, expect
-    assert B.pn_variant_name(17) not in names[1:]
+    assert B.pn_variant_name(18) not in names[1:]
     assert B.pn_variant_name(-1) not in names[1:]
 
 
@@ -157,6 +157,26 @@ def test_prefill_host_checks():
     big = 80 * 2 * 126_400  # pn3t, an even number of blocks, 256 rows x 8.6 MB
     assert call(K=big, ldx=big) == -4
     assert call(t=1, K=64 * 2 * 126_400, ldx=64 * 2 * 126_400) == -4
+
+
+def test_prefill_group_host_checks():
+    """pn_gemm_prefill_group: the count bounds, and each entry checked as
+    pn_gemm_prefill checks it, before anything is enqueued."""
+    lib = B.lib()
+    X16 = 0x10000
+    ok = ("pn3t", FAKE, 4, 640, X16, 640, 3, FAKE, 4)
+    assert lib.pn_gemm_prefill_group(None, 1, None) == PN_EINVAL
+    assert B.pn_gemm_prefill_group([], stream=0, check=False) == PN_EINVAL
+    assert B.pn_gemm_prefill_group([ok] * (B.PREFILL_GROUP_MAX + 1), stream=0, check=False) == PN_EINVAL
+    bad = [(("pn3t", FAKE, 4, 81, X16, 81, 3, FAKE, 4), PN_ESHAPE),
+           (("pn3t", FAKE, 4, 640, X16, 640, 0, FAKE, 4), PN_ESHAPE),
+           (("pn3t", FAKE, 4, 240, X16, 240, 3, FAKE, 4), -4),
+           (("pn3t", FAKE, 4, 640, X16 + 8, 640, 3, FAKE, 4), PN_EALIGN),
+           (("pn3t", FAKE, 4, 640, X16, 640, 3, None, 4), PN_EINVAL)]
+    for entry, status in bad:
+        # the failing entry last, after valid ones: still nothing runs
+        assert B.pn_gemm_prefill_group([ok, ok, entry], stream=0, check=False) == status, entry
+        assert B.pn_gemm_prefill_group([entry], stream=0, check=False) == status, entry
 
 
 def test_rotate_host_checks():

@@ -158,3 +158,84 @@ def test_prefill_dealing(case):
         for tile in range(whole):
             r0, c0 = (tile // tn) * 128, (tile % tn) * 256
             assert_bits_equal(y2[r0:r0 + 128, c0:c0 + 256], y[r0:r0 + 128, c0:c0 + 256], "tile %d dealt whole" % tile)
+
+
+def gpu_prefill_group(specs):
+    """Run (type, w, N, K, xm, ldx, ldy) products as one pn_gemm_prefill_group
+    launch; each product's outputs, checked for writes past N."""
+    probs, outs = [], []
+    for t, w, n, k, xm, ldx, ldy in specs:
+        m = xm.shape[0]
+        wd = dev(np.ascontiguousarray(w).reshape(-1))
+        xb = torch.zeros(m * ldx, dtype=torch.float16, device="cuda")
+        xb.view(m, ldx)[:, :k] = dev(xm)
+        y = torch.full((m * ldy,), float("nan"), dtype=torch.float32, device="cuda")
+        probs.append((t, wd, n, k, xb, ldx, m, y, ldy))
+        outs.append((y, m, n, ldy))
+    B.pn_gemm_prefill_group(probs)
+    sync()
+    assert B.pn_variant_name(B.pn_last_variant()) == "gemm_prefill_group"
+    res = []
+    for y, m, n, ldy in outs:
+        yh = y.view(m, ldy).cpu().numpy()
+        assert np.all(np.isnan(yh[:, n:])), "wrote past N"
+        res.append(yh[:, :n])
+    return res
+
+
+def check_group(specs, what):
+    for (t, w, n, k, xm, _, _), y in zip(specs, gpu_prefill_group(specs)):
+        y64, a = pnref.gemm_f64(t, w, n, k, xm)
+        assert_gemv_close(y, y64, a, "%s: %s %dx%d M=%d" % (what, t, n, k, xm.shape[0]))
+
+
+def group_specs(shapes, seed):
+    g = np.random.default_rng(seed)
+    specs = []
+    for t, n, k, m, ldx, ldy in shapes:
+        specs.append((t, synth.random_blocks(g, t, n, k, unused_bits=True), n, k, synth.activation(g, k, m),
+                      ldx or k, ldy or n))
+    return specs
+
+
+def test_prefill_group_mixed():
+    """One launch over products of both types, ragged N and M, different M
+    and K per product and padded leading dimensions: each against the
+    oracle."""
+    shapes = [("pn3t", 300, 640, 129, None, None), ("pn4t", 97, 1024, 129, 1032, 101),
+              ("pn4t", 260, 384, 40, None, None), ("pn3t", 33, 160, 5, 168, 40), ("pn3t", 513, 1280, 256, None, None)]
+    say("prefill group mixed: %d products" % len(shapes))
+    check_group(group_specs(shapes, 31), "prefill group mixed")
+
+
+@pytest.mark.parametrize("case", ["shared_across_products", "rounds_then_shared", "all_shared_mixed_pairs"])
+def test_prefill_group_dealing(case):
+    """The launch's tiles numbered product after product: whole rounds, then
+    the leftover tiles' block pairs shared where those tiles belong to
+    different products; and a launch below one round mixing pn3t (8 pairs
+    a tile) with pn4t (10 pairs), where the fewer pairs set the ways."""
+    G = cus()
+    shapes = {"shared_across_products": [("pn3t", (G - 2) * 256, 1280, 1, None, None),
+                                         ("pn4t", 3 * 256 - 50, 1280, 1, None, None),
+                                         ("pn3t", 256 + 9, 1280, 1, None, None)],
+              "rounds_then_shared": [("pn4t", G * 256, 1280, 1, None, None), ("pn3t", 300, 1280, 129, None, None)],
+              "all_shared_mixed_pairs": [("pn3t", (G // 8) * 256 - 5, 1280, 130, None, None),
+                                         ("pn4t", 256 + 3, 1280, 7, None, None)]}[case]
+    say("prefill group dealing %s on %d CUs" % (case, G))
+    check_group(group_specs(shapes, [41, G, len(case)]), "prefill group dealing %s" % case)
+
+
+def test_prefill_group_layer_full_size():
+    """A 27B-shaped layer's products in the groups a decoder can launch
+    together ({q, k, v} and {gate, up}; {o} and {down} alone), 512-token
+    chunk, as the benchmark runs them: every output against the oracle."""
+    m = 512
+    g = np.random.default_rng(23)
+    layer = synth.SWEEP_LAYER
+    for group in ((0, 1, 2), (4, 5)):
+        specs = []
+        for i in group:
+            name, t, n, k = layer[i]
+            specs.append((t, synth.random_blocks(g, t, n, k, unused_bits=True), n, k, synth.activation(g, k, m), k, n))
+        say("prefill group full size %s M=%d" % ("+".join(layer[i][0] for i in group), m))
+        check_group(specs, "prefill group full size")
