@@ -36,6 +36,8 @@ KERNEL_SOURCES = {
            "bit_quantized_decode_pn3t_amd/csrc/pn_device.h"],
     "smallm": ["bit_quantized_decode_pn3t_amd/csrc/pn_smallm.hip",
                "bit_quantized_decode_pn3t_amd/csrc/pn_device.h"],
+    "prefill": ["bit_quantized_decode_pn3t_amd/csrc/pn_prefill.hip",
+                "bit_quantized_decode_pn3t_amd/csrc/pn_device.h"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -227,7 +229,8 @@ def prefill_timing(B, synth, torch, m=512):
                                "tflops": round(flops / (single_ms * 1e-3) / 1e12, 1),
                                "note": "each product its own pn_gemm_prefill launch"},
             "groups": groups,
-            "per_matrix": per}
+            "per_matrix": per,
+            "kernel_hash": kernel_hash("prefill")}
 
 
 def layer_read_floor(B, torch, layers):

@@ -45,6 +45,40 @@ def test_prefill_split_k_graph_replays():
         assert_gemv_close(y.cpu().numpy(), y64, a, "prefill replay %d" % rep)
 
 
+def test_prefill_group_graph_replays():
+    """A grouped prefill launch (three products of both types, tiles shared
+    across products) captured into a graph: its arguments are captured by
+    value, so every replay recomputes the same products."""
+    specs = [("pn3t", 700, 1280, 150), ("pn4t", 300, 1280, 150), ("pn4t", 129, 2560, 33)]
+    host, probs = [], []
+    for i, (t, n, k, m) in enumerate(specs):
+        g = np.random.default_rng([43, i])
+        w = synth.random_blocks(g, t, n, k, unused_bits=True)
+        xm = synth.activation(g, k, m)
+        y64, a = pnref.gemm_f64(t, w, n, k, xm)
+        y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        host.append((t, n, m, y64, a, y))
+        probs.append((t, dev(w.reshape(-1)), n, k, dev(xm), k, m, y, n))
+    say("prefill group graph: eager")
+    B.pn_gemm_prefill_group(probs)
+    sync()
+    for t, n, m, y64, a, y in host:
+        assert_gemv_close(y.cpu().numpy(), y64, a, "prefill group eager %s N=%d" % (t, n))
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        B.pn_gemm_prefill_group(probs)
+    sync()
+    for rep in range(3):
+        say("prefill group graph: replay %d" % rep)
+        for *_, y in host:
+            y.fill_(float("nan"))  # eager work between the replays
+        sync()
+        gr.replay()
+        sync()
+        for t, n, m, y64, a, y in host:
+            assert_gemv_close(y.cpu().numpy(), y64, a, "prefill group replay %d %s N=%d" % (rep, t, n))
+
+
 def test_rotated_plan_graph_replays():
     specs = [("pn3t", 64, 5120), ("pn4t", 48, 6144), ("pn4t", 32, 17408)]
     host, probs = [], []
