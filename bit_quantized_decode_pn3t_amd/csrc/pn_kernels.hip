@@ -551,7 +551,8 @@ bool stream_v2(const Prob &p) { return (p.nw & 127) == 0; }
 // them, and workgroups take tiles in a grid stride.  Tiles are sized in
 // bytes, the same for every problem of a launch, so that the stride hands
 // every workgroup about the same amount of data: about 1/24 of a wave's
-// share of the launch, at least 16 KiB and at most 96 KiB per wave-tile.
+// share of the launch, at least 16 KiB (2 KiB in launches of at most 4 MiB,
+// which then spread over more waves) and at most 96 KiB per wave-tile.
 #ifndef PN_TILES_PER_WAVE
 #define PN_TILES_PER_WAVE 24
 #endif
@@ -563,6 +564,12 @@ constexpr int64_t kTilesPerWave = PN_TILES_PER_WAVE;
 #define PN_MIN_WAVE_TILE_KB 16
 #endif
 constexpr int64_t kMinWaveTileBytes = PN_MIN_WAVE_TILE_KB * 1024;
+// Launches of at most 4 MiB (the 256-row pn3t GEMV, a layer's k and v) take
+// wave-tiles down to 2 KiB: 256 x 5120 pn3t 9.9 -> 7.0 us a call, and the
+// per-matrix schedule's k and v calls faster too (1.297 -> 1.277 ms for 16
+// layers); larger launches are fastest at 16 KiB.
+constexpr int64_t kSmallLaunchBytes = 4 << 20;
+constexpr int64_t kSmallMinWaveTileBytes = 2 * 1024;
 constexpr int64_t kMaxWaveTileBytes = PN_MAX_WAVE_TILE_KB * 1024;
 
 int64_t row_bytes_of(const Prob &p) { return (int64_t)(p.nw >> 3) * 34; }
@@ -575,7 +582,8 @@ int64_t plan_tiles(Prob *probs, int count, int lds)
     int64_t bytes = 0;
     for (int i = 0; i < count; ++i) bytes += (int64_t)probs[i].N * row_bytes_of(probs[i]);
     int64_t target = bytes / (waves * kTilesPerWave);
-    if (target < kMinWaveTileBytes) target = kMinWaveTileBytes;
+    const int64_t floor_bytes = bytes <= kSmallLaunchBytes ? kSmallMinWaveTileBytes : kMinWaveTileBytes;
+    if (target < floor_bytes) target = floor_bytes;
     if (target > kMaxWaveTileBytes) target = kMaxWaveTileBytes;
     int64_t tiles = 0;
     for (int i = 0; i < count; ++i) {
