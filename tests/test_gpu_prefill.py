@@ -239,3 +239,23 @@ def test_prefill_group_layer_full_size():
             specs.append((t, synth.random_blocks(g, t, n, k, unused_bits=True), n, k, synth.activation(g, k, m), k, n))
         say("prefill group full size %s M=%d" % ("+".join(layer[i][0] for i in group), m))
         check_group(specs, "prefill group full size")
+
+
+def test_prefill_group_refuses_whole():
+    """A group with one bad entry is refused before anything runs: the good
+    entries' outputs stay untouched."""
+    g = np.random.default_rng(51)
+    t, n, k, m = "pn3t", 300, 640, 40
+    w = dev(synth.random_blocks(g, t, n, k).reshape(-1))
+    x = dev(synth.activation(g, k, m))
+    y = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
+    ybad = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
+    good = (t, w, n, k, x, k, m, y, n)
+    bad = (t, w, n, 81, x, k, m, ybad, n)  # K not a whole number of blocks
+    say("prefill group refused")
+    assert B.pn_gemm_prefill_group([good, bad], check=False) == -2
+    sync()
+    assert torch.isnan(y).all() and torch.isnan(ybad).all()
+    B.pn_gemm_prefill_group([good])
+    sync()
+    assert not torch.isnan(y).any()
