@@ -549,10 +549,19 @@ bool stream_v2(const Prob &p) { return (p.nw & 127) == 0; }
 // Tiles: a wave-tile is `rpw` consecutive rows of one problem (at most 64:
 // one result lane each; a multiple of kR), a workgroup-tile is kWaves of
 // them, and workgroups take tiles in a grid stride.  Tiles are sized in
-// bytes, the same for every problem of a launch, so that the stride hands
-// every workgroup about the same amount of data: about 1/24 of a wave's
-// share of the launch, at least 16 KiB (2 KiB in launches of at most 4 MiB,
-// which then spread over more waves) and at most 96 KiB per wave-tile.
+// bytes, the same target for every problem of a launch.
+//   Launches of up to 256 MiB (a layer's groups, single calls): the target
+//   whose tiles take the fewest rounds of the grid at the least cost,
+//   rounds x (largest wave-tile + 8 KiB for a tile's pipeline fill and
+//   drain).  Wave-tiles keep at least the rows for 2U pipelined items,
+//   except in launches of at most 1 MiB, where the smallest tiles spread
+//   the work widest.
+//   Larger launches: about 1/24 of a wave's share, 16-96 KiB.
+// Measured on one box (ms for a 16-layer sweep, graphs): the layer schedule
+// 0.974 -> 0.937 and the per-matrix one 1.278 -> 1.235 against the earlier
+// rule (1/24 of a share, at least 16 KiB); the 256-row pn3t GEMV 6.9 us
+// with 2-row tiles against 9.9 with 16 KiB ones and 7.8 with 4 rows; the
+// 47-76 MB single calls unchanged.
 #ifndef PN_TILES_PER_WAVE
 #define PN_TILES_PER_WAVE 24
 #endif
@@ -564,33 +573,67 @@ constexpr int64_t kTilesPerWave = PN_TILES_PER_WAVE;
 #define PN_MIN_WAVE_TILE_KB 16
 #endif
 constexpr int64_t kMinWaveTileBytes = PN_MIN_WAVE_TILE_KB * 1024;
-// Launches of at most 4 MiB (the 256-row pn3t GEMV, a layer's k and v) take
-// wave-tiles down to 2 KiB: 256 x 5120 pn3t 9.9 -> 7.0 us a call, and the
-// per-matrix schedule's k and v calls faster too (1.297 -> 1.277 ms for 16
-// layers); larger launches are fastest at 16 KiB.
-constexpr int64_t kSmallLaunchBytes = 4 << 20;
-constexpr int64_t kSmallMinWaveTileBytes = 2 * 1024;
 constexpr int64_t kMaxWaveTileBytes = PN_MAX_WAVE_TILE_KB * 1024;
+constexpr int64_t kBalancedMaxBytes = (int64_t)256 << 20;
+constexpr int64_t kTinyLaunchBytes = (int64_t)1 << 20;
+constexpr int64_t kTileFillBytes = 8 * 1024;
 
 int64_t row_bytes_of(const Prob &p) { return (int64_t)(p.nw >> 3) * 34; }
+
+// Rows of a wave-tile of about `target` bytes: a multiple of kR, at most 64,
+// and (pipelined) at least enough for 2U items of kR rows x one pass.
+int64_t tile_rows(int64_t target, const Prob &p, bool pipelined)
+{
+    int64_t lo = kR;
+    if (pipelined) {
+        const int64_t npass = p.nw / ((p.nw & 127) == 0 ? 128 : 64);
+        lo = (2 * kU * kR + npass - 1) / npass;
+        lo = (lo + kR - 1) / kR * kR;
+        if (lo < kR) lo = kR;
+        if (lo > 64) lo = 64;
+    }
+    int64_t rpw = (target / row_bytes_of(p) + kR / 2) / kR * kR;
+    if (rpw < lo) rpw = lo;
+    if (rpw > 64) rpw = 64;
+    return rpw;
+}
 
 // Set rpw and tile0 of every problem; returns the number of tiles, or -1.
 int64_t plan_tiles(Prob *probs, int count, int lds)
 {
     const DeviceInfo &d = device_info();
-    const int64_t waves = (int64_t)d.cus * stream_wgs_per_cu(d, lds) * kWaves;
+    const int64_t wgs = (int64_t)d.cus * stream_wgs_per_cu(d, lds);
+    const int64_t waves = wgs * kWaves;
     int64_t bytes = 0;
     for (int i = 0; i < count; ++i) bytes += (int64_t)probs[i].N * row_bytes_of(probs[i]);
-    int64_t target = bytes / (waves * kTilesPerWave);
-    const int64_t floor_bytes = bytes <= kSmallLaunchBytes ? kSmallMinWaveTileBytes : kMinWaveTileBytes;
-    if (target < floor_bytes) target = floor_bytes;
-    if (target > kMaxWaveTileBytes) target = kMaxWaveTileBytes;
+    const bool balanced = bytes <= kBalancedMaxBytes;
+    const bool pipelined = balanced && bytes > kTinyLaunchBytes;
+    int64_t target;
+    if (balanced) {
+        int64_t best_cost = INT64_MAX;
+        target = 2048;
+        for (int64_t t = 2048; t <= kMaxWaveTileBytes; t += 1024) {
+            int64_t n = 0, largest = 0;
+            for (int i = 0; i < count; ++i) {
+                const int64_t rpw = tile_rows(t, probs[i], pipelined);
+                n += ((int64_t)probs[i].N + kWaves * rpw - 1) / (kWaves * rpw);
+                if (rpw * row_bytes_of(probs[i]) > largest) largest = rpw * row_bytes_of(probs[i]);
+            }
+            const int64_t cost = (n + wgs - 1) / wgs * (largest + kTileFillBytes);
+            if (cost < best_cost) {
+                best_cost = cost;
+                target = t;
+            }
+        }
+    } else {
+        target = bytes / (waves * kTilesPerWave);
+        if (target < kMinWaveTileBytes) target = kMinWaveTileBytes;
+        if (target > kMaxWaveTileBytes) target = kMaxWaveTileBytes;
+    }
     int64_t tiles = 0;
     for (int i = 0; i < count; ++i) {
         Prob &p = probs[i];
-        int64_t rpw = (target / row_bytes_of(p) + kR / 2) / kR * kR;
-        if (rpw < kR) rpw = kR;
-        if (rpw > 64) rpw = 64;
+        const int64_t rpw = tile_rows(target, p, pipelined);
         p.rpw = (int32_t)rpw;
         p.tile0 = (int32_t)tiles;
         tiles += ((int64_t)p.N + kWaves * rpw - 1) / (kWaves * rpw);
