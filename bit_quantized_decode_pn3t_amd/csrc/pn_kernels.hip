@@ -96,7 +96,10 @@ struct StreamArgs {
 // kThreads entries, microseconds per problem for the long rows.  Buffer
 // loads (not global ones) keep the compiler's wait analysis of the weight
 // pipeline exact; entries past the end read zeros and are not written.
-constexpr int kStageBatch = 8;
+// Four entries a batch: eight made the staging the kernel's register peak
+// (88 VGPRs, five workgroups a CU, against 61 and eight), and the one-launch
+// layer groups and single calls ran 4-7 % slower for it.
+constexpr int kStageBatch = 4;
 
 template <int TYPE, int V>
 __device__ __forceinline__ void stage_x(const Prob &p, uint8_t *lds)
