@@ -15,6 +15,7 @@ pytestmark = pytest.mark.gpu
 
 from bit_quantized_decode_pn3t_amd import _binding as B  # noqa: E402
 from bit_quantized_decode_pn3t_amd import sweep as S  # noqa: E402
+from bit_quantized_decode_pn3t_amd import synth  # noqa: E402
 from oracle import pnref  # noqa: E402
 
 # the kernel each M = 1 schedule runs at these shapes
@@ -22,9 +23,10 @@ M1_VARIANT = {"token": "gemv_rows_group", "token_rot": "gemv_rows_group", "layer
               "gemv": "gemv_stream"}
 
 
-def oracle_rows(store, rotated=False):
+def oracle_rows(store, rotated=False, batch=None):
     """Callback for Sweep(sample=...): the oracle's y64 and sum|w x| for every
-    row of the matrix (and, with `rotated`, for its rotated input too)."""
+    row of the matrix (and, with `rotated`, for its rotated input too; with
+    `batch`, also for the M = batch activations that Sweep.batch_view draws)."""
     def sample(rec):
         key = (rec["layer"], rec["mat"])
         t, n, k, w, x = rec["type"], rec["N"], rec["K"], rec["W"], rec["x"]
@@ -34,6 +36,9 @@ def oracle_rows(store, rotated=False):
                 ent["rot"] = pnref.gemv_f64(t, w, n, k, pnref.rotate(x))
         else:
             ent = {"plain": pnref.gemm_f64(t, w, n, k, x)}
+        if batch:
+            xb = synth.activation(synth.rng(4, rec["layer"], rec["mat"]), k, batch)
+            ent["batch"] = pnref.gemm_f64(t, w, n, k, xb)
         store[key] = ent
     return sample
 
@@ -101,8 +106,8 @@ def sweep_m8():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     store = {}
-    say("sweep M=8: generating 64 layers and the oracle's rows")
-    sw = S.Sweep(m=8, sample=oracle_rows(store), unused_bits=True)
+    say("sweep M=8: generating 64 layers and the oracle's rows (M = 8 and 16)")
+    sw = S.Sweep(m=8, sample=oracle_rows(store, batch=16), unused_bits=True)
     yield sw, store
     sw.close()
     del sw
@@ -134,3 +139,23 @@ def test_sweep_m8(sweep_m8, math):
         B.pn_set_smallm_math("mfma")
         B.pn_set_gemv_kernel("auto")
         sw.close()
+
+
+def test_sweep_m16(sweep_m8):
+    """M = 16 (the widest small-batch tile) over the full sweep, one grouped
+    launch per token on the same resident weights: every one of the 54.5 M
+    outputs against the oracle."""
+    sw, store = sweep_m8
+    v = sw.batch_view(16)
+    try:
+        for e in v.mats:
+            e["y"].fill_(float("nan"))
+        say("sweep M=16 token schedule")
+        v.step("token")
+        sync()
+        assert B.pn_variant_name(B.pn_last_variant()) == "gemm_rows_mfma_group"
+        worst, rows = check_all_rows(v, store, "batch")
+        assert rows == 16 * 64 * (6144 + 2 * 1024 + 5120 + 2 * 17408 + 5120)
+        say("sweep M=16: %d outputs, worst %.3g" % (rows, worst))
+    finally:
+        v.close()
