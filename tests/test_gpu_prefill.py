@@ -259,3 +259,13 @@ def test_prefill_group_refuses_whole():
     B.pn_gemm_prefill_group([good])
     sync()
     assert not torch.isnan(y).any()
+
+
+def test_prefill_group_eight():
+    """The largest group (PN_PREFILL_GROUP_MAX products), small shapes of
+    both types: every tile finds its product among all eight records."""
+    assert B.PREFILL_GROUP_MAX == 8
+    shapes = [("pn3t" if i % 2 else "pn4t", 40 + 67 * i, 640 if i % 2 else 512, 17 + 23 * i, None, None)
+              for i in range(8)]
+    say("prefill group of 8")
+    check_group(group_specs(shapes, 61), "prefill group of 8")
