@@ -89,47 +89,36 @@ struct StreamArgs {
 // to a 4-byte entry in a second array (one ds_read_b128 + one ds_read_b32,
 // both aligned).  LDS bytes: 16*nw (+ 4*nw for pn3t) = 2*K.
 // ---------------------------------------------------------------------------
-// Threads walk LDS entries in order (conflict-free stores); entry e of slot
-// v holds word f = V * (e - v * per) + v.  Each thread issues the loads of up
-// to kStageBatch entries before it writes any of them: a loop that waited
-// for every entry's load before the next took one memory round trip per
-// kThreads entries, microseconds per problem for the long rows.  Buffer
-// loads (not global ones) keep the compiler's wait analysis of the weight
-// pipeline exact; entries past the end read zeros and are not written.
-// Four entries a batch: eight made the staging the kernel's register peak
-// (88 VGPRs, five workgroups a CU, against 61 and eight), and the one-launch
-// layer groups and single calls ran 4-7 % slower for it.
-constexpr int kStageBatch = 4;
-
+// Entry e of slot v holds word f = V * (e - v * per) + v.  The entries are
+// filled by DMA (buffer_load ... lds, 16 bytes a lane, plus 4 for pn3t's
+// second array): lane l of instruction i fetches entry 64 i + l, so the
+// instruction writes 1 KiB (256 bytes) of LDS in order, and no register
+// holds the activation on its way.  The workgroup's waves issue its
+// instructions round-robin, all at once, and a wave issues its first weight
+// loads right behind them; it waits for its own DMA and meets the others at
+// a barrier only then, so the activation's latency hides under the
+// weights'.  (Staged through registers, four entries in flight a thread,
+// the staging made the kernel's register peak, and one round trip a batch
+// came before the first weight load: the layer schedule 0.883 vs 0.842 ms
+// per 16 layers, the per-matrix schedule 1.148 vs 1.073, the single calls
+// 3-6 % slower.  Eight entries a batch took 88 VGPRs and five workgroups a
+// CU.)  Needs nw % 64 == 0: whole instructions, none writing past the
+// arrays.  The caller waits (vmcnt) and synchronises before any read.
+typedef __attribute__((address_space(3))) void lds_void_t;
 template <int TYPE, int V>
-__device__ __forceinline__ void stage_x(const Prob &p, uint8_t *lds)
+__device__ __forceinline__ void stage_x_dma(const Prob &p, uint8_t *lds, int wave, int lane)
 {
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     constexpr int kEntry = TYPE == 0 ? 20 : 16;  // activation bytes per word
     const int nw = p.nw;
     const int per = nw / V;  // entries per slot
-    u32x4 *a = (u32x4 *)lds;
-    uint32_t *b = (uint32_t *)(lds + 16 * nw);
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(uniform_ptr(p.x), (uint32_t)(kEntry * nw));
-    for (int e0 = 0; e0 < nw; e0 += kStageBatch * kThreads) {
-        u32x4 va[kStageBatch];
-        uint32_t vb[kStageBatch];
-#pragma unroll
-        for (int k = 0; k < kStageBatch; ++k) {
-            const int e = e0 + k * kThreads + (int)threadIdx.x;
-            const int v = e / per;
-            const int off = kEntry * (V * (e - v * per) + v);
-            va[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
-            if constexpr (TYPE == 0) vb[k] = __builtin_amdgcn_raw_buffer_load_b32(xr, off + 16, 0, 0);
-        }
-#pragma unroll
-        for (int k = 0; k < kStageBatch; ++k) {
-            const int e = e0 + k * kThreads + (int)threadIdx.x;
-            if (e < nw) {
-                a[e] = va[k];
-                if constexpr (TYPE == 0) b[e] = vb[k];
-            }
-        }
+    for (int i = wave; i < nw / 64; i += kWaves) {
+        const int e = 64 * i + lane;
+        const int v = e / per;
+        const int off = kEntry * (V * (e - v * per) + v);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t *)(lds + 1024 * i), 16, off, 0, 0, 0);
+        if constexpr (TYPE == 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t *)(lds + 16 * nw + 256 * i), 4, off + 16, 0, 0, 0);
     }
 }
 
@@ -146,10 +135,13 @@ __device__ __forceinline__ uint32_t scale_off(uint32_t f) { return 34u * (f >> 3
 // load stream never drains until the wave's last row.  All loads go through
 // one buffer resource that covers the wave's valid rows: rows past N read
 // zeros (no clamping, no fault).  Finished row sums are parked in lane
-// (row - row0) of one register and stored once at the end.
+// (row - row0) of one register and stored once at the end.  With `restage`
+// the workgroup's activation DMA was issued just before: the wave waits for
+// it behind its first weight loads and meets the other waves at a barrier
+// (a wave without rows, nrows = 0, only waits and meets them).
 // Requires nw % (64 * V) == 0.
 template <int TYPE, int R, int U, int V>
-__device__ __forceinline__ void stream_wave(const Prob &p, int row0, int nrows, const uint8_t *lds)
+__device__ __forceinline__ void stream_wave(const Prob &p, int row0, int nrows, const uint8_t *lds, bool restage)
 {
     constexpr int P = Unpack<TYPE>::kPairs;
     constexpr int kPassBytes = 8 * V * kBlockBytes;  // 272 * V
@@ -157,7 +149,8 @@ __device__ __forceinline__ void stream_wave(const Prob &p, int row0, int nrows, 
     const int nw = uniform(p.nw);
     const int npass = nw / (64 * V);
     const int row_bytes = uniform((nw >> 3) * 34);
-    const int valid = uniform(p.N - row0 < nrows ? p.N - row0 : nrows);
+    const int valid0 = uniform(p.N - row0 < nrows ? p.N - row0 : nrows);
+    const int valid = valid0 < 0 ? 0 : valid0;
     const int total = uniform(((nrows + R - 1) / R) * npass);
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc(uniform_ptr(p.W + (size_t)row0 * row_bytes), (uint32_t)valid * (uint32_t)row_bytes);
@@ -254,6 +247,15 @@ __device__ __forceinline__ void stream_wave(const Prob &p, int row0, int nrows, 
         // covers only its own loads.
 #pragma unroll
         for (int u = 0; u < U; ++u) issue(u);
+        if (restage) {
+            // the activation's DMA (issued before these loads) has landed for
+            // this wave; after the barrier, for every wave
+            constexpr int kPro = U * R * 2;
+            __builtin_amdgcn_s_waitcnt((((kPro >> 4) & 3) << 14) | 0x0f70 | (kPro & 15));
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        }
         int done = 0;
         do {
 #pragma unroll
@@ -275,6 +277,12 @@ __device__ __forceinline__ void stream_wave(const Prob &p, int row0, int nrows, 
         for (int u = 0; u < U; ++u)
             if (done + U + u < total) consume(u);
     } else {
+        if (restage) {
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        }
         for (int i = 0; i < total; ++i) {
             issue(0);
             consume(0);
@@ -314,6 +322,7 @@ __global__ __launch_bounds__(kThreads) void gemv_stream(StreamArgs args)
     int i = 0;
     int next0 = -1;  // first tile of problem i + 1; -1 before the first problem
     Prob p;
+    bool restage = false;
     for (int tile = blockIdx.x; tile < args.total_tiles; tile += gridDim.x) {
         if (tile >= next0) {
             // advance to the problem holding this tile (tiles only move forward)
@@ -329,20 +338,24 @@ __global__ __launch_bounds__(kThreads) void gemv_stream(StreamArgs args)
             p.tile0 = uniform(c.tile0);
             p.rpw = uniform(c.rpw);
             next0 = uniform(problem_tile0(args, i + 1));
+            restage = true;
+            // every wave is done reading the previous activation
             __syncthreads();
             if (p.type == 0)
-                stage_x<0, V>(p, lds);
+                stage_x_dma<0, V>(p, lds, wave, (int)(threadIdx.x & 63));
             else
-                stage_x<1, V>(p, lds);
-            __syncthreads();
+                stage_x_dma<1, V>(p, lds, wave, (int)(threadIdx.x & 63));
         }
         const int row0 = ((tile - p.tile0) * kWaves + wave) * p.rpw;
-        if (row0 < p.N) {
+        // waves without rows still wait for the staging with the others
+        if (row0 < p.N || restage) {
+            const int nrows = row0 < p.N ? p.rpw : 0;
             if (p.type == 0)
-                stream_wave<0, R, U, V>(p, row0, p.rpw, lds);
+                stream_wave<0, R, U, V>(p, row0, nrows, lds, restage);
             else
-                stream_wave<1, R, U, V>(p, row0, p.rpw, lds);
+                stream_wave<1, R, U, V>(p, row0, nrows, lds, restage);
         }
+        restage = false;
     }
 }
 
