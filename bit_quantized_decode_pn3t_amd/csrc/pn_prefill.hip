@@ -99,10 +99,13 @@ struct Pf {
     static constexpr int XDMA = kPfM * XSL / 64;      // X DMA instructions per stage
     static constexpr int XBYTES = 1024 * XDMA;
     static constexpr int WDMA = kPfN * kPairDw / 64;  // W DMA instructions (4 bytes a lane)
-    static constexpr int STAGE = XBYTES + 256 * WDMA;
+    static constexpr int WBYTES = 256 * WDMA;
     static constexpr int XPER = (XDMA + kPfWaves - 1) / kPfWaves;  // X DMA instructions per wave (at most)
     static constexpr int WPER = (WDMA + kPfWaves - 1) / kPfWaves;
-    static constexpr int LDS = 2 * STAGE;
+    static constexpr int WSTAGES = 3;  // weight stages: two pairs of lookahead from HBM
+    static constexpr int LDS = 2 * XBYTES + WSTAGES * WBYTES;
+    // this wave's weight DMA instructions per pair (round-robin over the waves)
+    static constexpr int wcount(int wave) { return (WDMA - wave + kPfWaves - 1) / kPfWaves; }
     static_assert(kPfM * XSL % 64 == 0 && kPfN * kPairDw % 64 == 0, "whole DMA instructions");
 };
 
@@ -210,25 +213,46 @@ __device__ __forceinline__ void pf_offsets(uint32_t (&xo)[Pf<TYPE>::XPER], uint3
 }
 
 template <int TYPE>
-__device__ __forceinline__ void stage_pair(uint8_t *st, const __amdgpu_buffer_rsrc_t &xr, const __amdgpu_buffer_rsrc_t &wr,
-                                           const uint32_t (&xo)[Pf<TYPE>::XPER], const uint32_t (&wo)[Pf<TYPE>::WPER],
-                                           int p, int wave)
+__device__ __forceinline__ void stage_x(uint8_t *st, const __amdgpu_buffer_rsrc_t &xr, const uint32_t (&xo)[Pf<TYPE>::XPER],
+                                       int p, int wave)
 {
     using C = Pf<TYPE>;
-    const int xso = p * C::KS * 2, wso = p * 68;
+    const int xso = p * C::KS * 2;
 #pragma unroll
     for (int t = 0; t < C::XPER; ++t) {
         const int i = wave + kPfWaves * t;
         if (i < C::XDMA)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)(st + 1024 * i), 16, (int)xo[t], xso, 0, 0);
     }
+}
+
+template <int TYPE>
+__device__ __forceinline__ void stage_w(uint8_t *st, const __amdgpu_buffer_rsrc_t &wr, const uint32_t (&wo)[Pf<TYPE>::WPER],
+                                       int p, int wave)
+{
+    using C = Pf<TYPE>;
+    const int wso = p * 68;
 #pragma unroll
     for (int t = 0; t < C::WPER; ++t) {
         const int i = wave + kPfWaves * t;
         if (i < C::WDMA)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void *)(st + C::XBYTES + 256 * i), 4, (int)wo[t], wso, 0,
-                                                     0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void *)(st + 256 * i), 4, (int)wo[t], wso, 0, 0);
     }
+}
+
+// Wait until at most n of this wave's loads are outstanding (n = 0 or one
+// pair's weight DMA count).
+template <int TYPE>
+__device__ __forceinline__ void pf_wait_vm(bool keep_w, int wave)
+{
+    using C = Pf<TYPE>;
+    static_assert(C::wcount(0) < 16 && C::wcount(kPfWaves - 1) + 1 >= C::wcount(0), "vmcnt immediates");
+    if (!keep_w)
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    else if (C::wcount(wave) == C::wcount(0))
+        __builtin_amdgcn_s_waitcnt(0x0f70 | C::wcount(0));
+    else
+        __builtin_amdgcn_s_waitcnt(0x0f70 | C::wcount(kPfWaves - 1));
 }
 
 // Block pairs [p0, p1) of tile u of product a (N tile u % tn, M tile u / tn),
@@ -257,18 +281,34 @@ __device__ __forceinline__ void pf_piece(const PfProb &a, int u, int p0, int p1,
 #pragma unroll
         for (int j = 0; j < kNT; ++j) acc[i][j] = (float16_t){};
 
+    // LDS: two X stages, then WSTAGES weight stages.  Pair j of the piece
+    // uses X stage j % 2 and weight stage j % WSTAGES; at its top the wave
+    // issues pair j + 1's X and pair j + 2's weights, so a weight DMA has
+    // two pairs' compute to land and an X DMA (mostly from L2) one.
+    uint8_t *const wbase = lds + 2 * C::XBYTES;
     // every wave is done with the stages of the workgroup's last piece
     __syncthreads();
-    stage_pair<TYPE>(lds, xr, wr, xo, wo, p0, wave);
+    stage_x<TYPE>(lds, xr, xo, p0, wave);
+    stage_w<TYPE>(wbase, wr, wo, p0, wave);
+    if (p0 + 1 < p1) stage_w<TYPE>(wbase + C::WBYTES, wr, wo, p0 + 1, wave);
+    int wcur = 0;  // (p - p0) % WSTAGES
     for (int p = p0; p < p1; ++p) {
-        // this wave's loads of pair p have landed; after the barrier, every
-        // wave's have, and every wave is done with pair p - 1's stage
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-        __syncthreads();
-        uint8_t *st = lds + ((p - p0) & 1) * C::STAGE;
-        if (p + 1 < p1) stage_pair<TYPE>(lds + ((p - p0 + 1) & 1) * C::STAGE, xr, wr, xo, wo, p + 1, wave);
-        const uint16_t *xs = (const uint16_t *)st;
-        const uint32_t *ws = (const uint32_t *)(st + C::XBYTES);
+        // this wave's loads of pair p have landed (pair p + 1's weights, the
+        // youngest, may still be in flight); after the barrier, every wave's
+        // have, and every wave is done with pair p - 1's stages
+        pf_wait_vm<TYPE>(p + 1 < p1, wave);
+        // a bare barrier: __syncthreads() would also wait for the weight
+        // DMA still in flight.  The stage's DMA is complete (the waits), and
+        // every wave has consumed its reads of the stages being refilled.
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        const int wnext2 = wcur + 2 < C::WSTAGES ? wcur + 2 : wcur + 2 - C::WSTAGES;
+        if (p + 1 < p1) stage_x<TYPE>(lds + ((p - p0 + 1) & 1) * C::XBYTES, xr, xo, p + 1, wave);
+        if (p + 2 < p1) stage_w<TYPE>(wbase + wnext2 * C::WBYTES, wr, wo, p + 2, wave);
+        const uint16_t *xs = (const uint16_t *)(lds + ((p - p0) & 1) * C::XBYTES);
+        const uint32_t *ws = (const uint32_t *)(wbase + wcur * C::WBYTES);
+        wcur = wcur + 1 < C::WSTAGES ? wcur + 1 : 0;
 
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
