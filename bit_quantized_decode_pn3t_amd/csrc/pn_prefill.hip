@@ -21,9 +21,9 @@
 // every weight row is decoded by one wave only.  The K loop takes one block
 // pair (two 34-byte blocks, 68 bytes, 17 aligned dwords: 160 k for pn3t,
 // 128 for pn4t) at a time: the workgroup stages the X tile (128 x 160 or
-// 128 fp16) and the 256 weight rows' block pairs in LDS by DMA, into one of
-// two stages while the other is computed, and each wave decodes its 32
-// weight rows straight into B operands.
+// 128 fp16) and the 256 weight rows' block pairs in LDS by DMA (X one pair
+// ahead in two stages, the weights two pairs ahead in three), and each wave
+// decodes its 32 weight rows straight into B operands.
 //
 // Work.  One launch takes one product or several (up to 8, of either type,
 // numbered one after another: a decoder layer's q, k and v, or gate and
@@ -467,7 +467,7 @@ pn_status pf_make(pn_type t, const void *W, int64_t N, int64_t K, const void *X,
 int64_t pf_tiles(const PfProb &p) { return (int64_t)p.tn * ((p.M + kPfM - 1) / kPfM); }
 
 // Number the products' tiles one after another, deal them and launch.  One
-// workgroup per CU (the two LDS stages take 102-118 KiB): the tiles of whole
+// workgroup per CU (its LDS stages take 122-138 KiB): the tiles of whole
 // rounds are dealt whole, and the R others are each shared by `ways`
 // workgroups, as many as fit one round, at most 8 and with at least 4 block
 // pairs of every product each: the atomic adds of a shared tile cost about
