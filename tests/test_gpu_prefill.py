@@ -35,9 +35,12 @@ def gpu_prefill(t, w, n, k, xm, ldx=None, ldy=None):
 
 
 # (type, N, K, M): tiles of 128 x 128, ragged in both; K from one block pair per
-# period to the down projection's 17408
+# period to the down projection's 17408, with rows of two and three block
+# pairs (the weights run two pairs ahead of the pair computed: pieces of one,
+# two and three pairs take different paths through the pipeline)
 SHAPES = [("pn3t", 256, 5120, 1), ("pn3t", 256, 5120, 17), ("pn3t", 256, 5120, 300), ("pn4t", 320, 6144, 129),
-          ("pn4t", 130, 17408, 64), ("pn3t", 1000, 640, 257), ("pn4t", 96, 128, 200), ("pn3t", 33, 160, 5)]
+          ("pn4t", 130, 17408, 64), ("pn3t", 1000, 640, 257), ("pn4t", 96, 128, 200), ("pn3t", 33, 160, 5),
+          ("pn4t", 300, 256, 140), ("pn3t", 270, 480, 33)]
 
 
 @pytest.mark.parametrize("t,n,k,m", SHAPES)
