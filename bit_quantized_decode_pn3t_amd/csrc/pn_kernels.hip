@@ -249,8 +249,11 @@ __device__ __forceinline__ void stream_wave(const Prob &p, int row0, int nrows, 
         for (int u = 0; u < U; ++u) issue(u);
         if (restage) {
             // the activation's DMA (issued before these loads) has landed for
-            // this wave; after the barrier, for every wave
-            constexpr int kPro = U * R * 2;
+            // this wave; after the barrier, for every wave.  The prologue's
+            // loads: one per row and item with the scale in the words'
+            // window, else two (words, scale).
+            constexpr int kPro = U * R * (kSiw ? 1 : 2);
+            static_assert(kPro < 64, "vmcnt immediate");
             __builtin_amdgcn_s_waitcnt((((kPro >> 4) & 3) << 14) | 0x0f70 | (kPro & 15));
             asm volatile("" ::: "memory");
             __builtin_amdgcn_s_barrier();
