@@ -290,6 +290,7 @@ __device__ __forceinline__ void pf_piece(const PfProb &a, int u, int p0, int p1,
     __syncthreads();
     stage_x<TYPE>(lds, xr, xo, p0, wave);
     stage_w<TYPE>(wbase, wr, wo, p0, wave);
+    asm volatile("" ::: "memory");
     if (p0 + 1 < p1) stage_w<TYPE>(wbase + C::WBYTES, wr, wo, p0 + 1, wave);
     int wcur = 0;  // (p - p0) % WSTAGES
     for (int p = p0; p < p1; ++p) {
@@ -305,6 +306,8 @@ __device__ __forceinline__ void pf_piece(const PfProb &a, int u, int p0, int p1,
         asm volatile("" ::: "memory");
         const int wnext2 = wcur + 2 < C::WSTAGES ? wcur + 2 : wcur + 2 - C::WSTAGES;
         if (p + 1 < p1) stage_x<TYPE>(lds + ((p - p0 + 1) & 1) * C::XBYTES, xr, xo, p + 1, wave);
+        // the weight DMA stays the youngest: the next pair's wait counts on it
+        asm volatile("" ::: "memory");
         if (p + 2 < p1) stage_w<TYPE>(wbase + wnext2 * C::WBYTES, wr, wo, p + 2, wave);
         const uint16_t *xs = (const uint16_t *)(lds + ((p - p0) & 1) * C::XBYTES);
         const uint32_t *ws = (const uint32_t *)(wbase + wcur * C::WBYTES);
