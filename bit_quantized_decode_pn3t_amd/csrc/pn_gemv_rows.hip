@@ -153,6 +153,7 @@ struct RArgs {
     RProb p0, p1;                  // inline problems (pn_gemv, pn_gemv2)
     int32_t count;                 // problems
     int32_t total_tiles;           // tiles of the launch
+    int32_t step_cap;              // steps no wave of a correct run reaches
 };
 
 template <int I, int N, typename F>
@@ -696,8 +697,14 @@ __global__ __launch_bounds__(kRThreads) void gemv_rows(RArgs a)
                 issue_x(ci, ci.type == 0 ? xl3 : xl4, xs, sl);
             }
         };
+        // A wave's steps are its windows, grabs and scans, all bounded in a
+        // correct run (pool counters only grow); the cap ends the loop all the
+        // same if the counters were disturbed, e.g. by a plan run concurrently
+        // with itself, so that the launch ends with wrong sums instead of
+        // never ending.
+        int32_t steps = 0;
         for (;;) {
-            if (sl0.done) break;
+            if (sl0.done || (steps += 2) > a.step_cap) break;
             step(ring, xs0, sl0, xs1, sl1);
             if (sl1.done) break;
             step(ring + (kNS - 1) * kStage, xs1, sl1, xs0, sl0);
@@ -789,6 +796,14 @@ __global__ __launch_bounds__(256) void rows_batch_setup(RBatch b, uint8_t *buf)
     for (int j = tid; j < (int)(kBatchCounterBytes / 4); j += stride) counters[j] = 0u;
 }
 
+// More steps than any wave of a correct launch takes: every window of the
+// launch, a grab or scan per tile and per pool, and the pipeline's ends.
+int32_t step_cap(int64_t total_tiles, int maxwin)
+{
+    const int64_t c = total_tiles * (int64_t)(maxwin + 2) + 2 * kPools + 8;
+    return c < INT32_MAX ? (int32_t)c : INT32_MAX;
+}
+
 pn_status rlaunch(const RArgs &a, hipStream_t s, int variant)
 {
     if (!once_per_device(kAttrRows, set_rows_attr)) return PN_ELAUNCH;
@@ -837,6 +852,7 @@ pn_status pn::host::rows_launch(int t, const void *W0, const void *W1, int64_t N
         a.count = 2;
         a.total_tiles += a.p1.tiles;
     }
+    a.step_cap = step_cap(a.total_tiles, a.p0.nwin);
     return rlaunch(a, s, kVarRows);
 }
 
@@ -907,6 +923,7 @@ pn_status pn::host::rows_group_create(const pn_gemv_desc *descs, int count, pn_g
     g->device = current_device();
     g->count = count;
     g->total_tiles = (int)total;
+    g->max_win = maxwin;
     g->lds = kRing;
     g->flags = (int)coff;  // byte offset of the counters
     *out = g;
@@ -922,6 +939,7 @@ pn_status pn::host::rows_group_run(const pn_group *g, hipStream_t s)
     a.counters = (uint32_t *)((uint8_t *)g->table + g->flags);
     a.count = g->count;
     a.total_tiles = g->total_tiles;
+    a.step_cap = step_cap(g->total_tiles, g->max_win);
     return rlaunch(a, s, kVarGroupRows);
 }
 
@@ -963,5 +981,6 @@ pn_status pn::host::rows_batch_launch(const pn_gemv_desc *descs, int count, uint
     a.counters = (uint32_t *)buf;
     a.count = count;
     a.total_tiles = (int32_t)total;
+    a.step_cap = step_cap(total, maxwin);
     return rlaunch(a, s, kVarBatchRows);
 }

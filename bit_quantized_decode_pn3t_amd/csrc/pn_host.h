@@ -98,6 +98,7 @@ struct pn_group {
     void *rot;          // problems with rotated inputs: RotJob list, then the rotated copies
     int rot_jobs;       // 1024-element blocks to rotate before the GEMV launch (0: none)
     int device;         // device current at creation: the plan's memory lives there
+    int max_win;        // gemv_rows plans: most windows in one tile (bounds a wave's steps)
 };
 
 namespace pn {

@@ -908,6 +908,12 @@ __global__ __launch_bounds__(kDmThreads) void gemm_rows(SmArgs args)
     int row0 = ((t - p.tile0) * kDmWaves + wave) * kDmRows;
     DmSrc d = dm_src(p, row0);
     dm_issue(d, 0, ring, rr, cc, lane);
+    // Each pass computes one tile, and a workgroup of a correct run computes
+    // at most every tile of the launch (grabbed groups only grow); the cap ends
+    // the loop all the same if the plan's counter was disturbed, e.g. by a
+    // plan run concurrently with itself.  It is the same for every wave of the
+    // workgroup, so they leave together.
+    int passes = 0;
     for (;;) {
         // the next tile (of this group, or the first of the next), looked up
         // ahead so that its first stage can be issued early
@@ -936,7 +942,7 @@ __global__ __launch_bounds__(kDmThreads) void gemm_rows(SmArgs args)
             dm_tile<0>(p, row0, d, dn, tn >= 0, lds, ring, rr, cc);
         else
             dm_tile<1>(p, row0, d, dn, tn >= 0, lds, ring, rr, cc);
-        if (tn < 0) break;
+        if (tn < 0 || ++passes >= args.total_tiles) break;
         if (ts >= 0) {
             ++sub;
         } else {

@@ -32,7 +32,9 @@
  * two exceptions.  A group plan must not run concurrently with itself (two
  * runs of one plan on different streams, or graph launches of it that
  * overlap): some plans keep tile counters in the plan's device memory, and
- * two runs sharing them would each compute only part of the output.  And a
+ * two runs sharing them would each compute only part of the output.  (Such
+ * runs still end: each wave or workgroup stops after more steps than any
+ * correct run takes, and the outputs are then unspecified.)  And a
  * plan must not be destroyed while another thread runs it.  The kernel
  * selections (pn_set_gemv_kernel, pn_set_smallm_math) belong to the calling
  * host thread, and the variant census (pn_last_variant) too.  Per-device
