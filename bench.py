@@ -146,7 +146,7 @@ def per_config_timing(B, synth, torch):
 PEAK_TFLOPS_F16 = 2500.0  # MI355X dense fp16 MFMA, AMD's published figure
 
 
-def prefill_timing(B, synth, torch, m=512):
+def prefill_timing(B, synth, torch, m=512, layer_only=False):
     """Prefill of one 27B-shaped decoder layer (q, k, v, o, gate, up, down;
     weights decoded inside the MFMA GEMM) for an m-token prompt chunk, in
     the four launches a decoder can make in dependency order: {q, k, v} and
@@ -155,7 +155,8 @@ def prefill_timing(B, synth, torch, m=512):
     queued back to back behind a short spin kernel (so that the host's issue
     time is not measured), HIP events around them, median of 10.  The seven
     products one launch each, and each product alone, are timed the same
-    way.  Flops = 2 m N K per product."""
+    way.  Flops = 2 m N K per product.  layer_only: the four launches only
+    (13 layers: 3 untimed, 10 timed), for the counter runs."""
     import numpy as np
     from bit_quantized_decode_pn3t_amd.sweep import LAYER_GROUPS
     dev = torch.device("cuda")
@@ -168,6 +169,8 @@ def prefill_timing(B, synth, torch, m=512):
         y = torch.empty((m, n), dtype=torch.float32, device=dev)
         mats.append((name, t, n, k, w, x, y))
         flops += 2 * m * n * k
+    # each product reads its weights and its X once and writes its Y once
+    algo = sum(w.numel() + 2 * m * k + 4 * m * n for _, t, n, k, w, x, y in mats)
 
     def call(e):
         name, t, n, k, w, x, y = e
@@ -201,6 +204,9 @@ def prefill_timing(B, synth, torch, m=512):
                 B.pn_gemm_prefill_group([(t, w, n, k, x, k, m, y, n)
                                          for _, t, n, k, w, x, y in (mats[i] for i in grp)])
 
+    if layer_only:
+        total_ms = queued(grouped)
+        return {"ms_per_layer": round(total_ms, 4), "layers_run": 13, "algorithmic_bytes_per_layer": algo}
     per = {}
     for e in mats:
         ms = queued(lambda: call(e))
@@ -222,7 +228,9 @@ def prefill_timing(B, synth, torch, m=512):
             "ms_per_layer": round(total_ms, 4), "tflops": round(tf, 1),
             "tokens_per_s_64_layers": round(m / (64 * total_ms * 1e-3), 1),
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_TFLOPS_F16, "unit": "TFLOP/s",
-                         "frac": round(tf / PEAK_TFLOPS_F16, 4), "traffic": None,
+                         "frac": round(tf / PEAK_TFLOPS_F16, 4),
+                         "traffic": measured_traffic("prefill_layer_m512", "prefill"),
+                         "algorithmic_bytes_per_layer": algo,
                          "kernel": "gemm_prefill",
                          "note": "the layer's four launches queued back to back, events around the four"},
             "seven_launches": {"ms_per_layer": round(single_ms, 4),
@@ -392,6 +400,8 @@ def main():
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the other schedules")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the prefill layer's four launches (for counter runs); prints their JSON")
     ap.add_argument("--cpu-layers", type=int, default=None,
                     help="layers in the oracle's sample (default 64 at M=1, 8 at M=8)")
     ap.add_argument("--no-configs", action="store_true",
@@ -422,6 +432,9 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: %d bytes read, %d written" % (n, n))
         del src, dst
+    if args.prefill_only:
+        print(json.dumps({"prefill": prefill_timing(B, synth, torch, layer_only=True)}), flush=True)
+        return
     m = None if args.config == 3 else args.m
     schedule = args.schedule
     if m is not None and schedule == "layer":
